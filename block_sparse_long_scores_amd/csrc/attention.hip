@@ -1,0 +1,494 @@
+// Block-sparse (and dense) causal prefill attention with mean correction, gfx950.
+//
+// Source: "FlashPrefill V2: block-sparse prefill attention for long-context LLM
+// serving", abstract (sparse attention operator with PackGQA memory access,
+// FP8, paged KV cache, mean correction term), and the papers.ananclaw.com
+// explainer §2.1 (query block q computes only Supp(q); Out_q^V2 adds the
+// dropped blocks' mass through mu_q and their average value) and §2.2
+// (PackGQA).  The pages' kernel targets Hopper (warp specialization, pingpong);
+// this one is laid out for CDNA4 instead:
+//
+//  * One workgroup per (sequence, KV head h, query block i, part): its 4
+//    wavefronts hold 256 of the G query heads x b rows of the GQA group, 64
+//    packed query rows per wave (PackGQA: every query head of the group reads
+//    the same K/V tile from LDS; a 512-row group takes two workgroups, which
+//    land on the same XCD and share its L2).
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: keys on the M side, queries on
+//    the N side, so each lane owns 2 query columns and the row max / row sum
+//    of the online softmax are lane-local plus one permlane32 exchange.
+//  * The accumulator registers of S^T, in order, are the B-operand slots of
+//    the P V MFMA (4 consecutive keys per half-slot), so P^T feeds
+//    v_mfma_f32_32x32x16_bf16 straight from registers; O^T = V^T P^T
+//    accumulates in the AGPR file.  The V^T operand comes from
+//    ds_read_b64_tr_b16 (LDS transpose read: 4 consecutive keys of one d per
+//    lane) on the natural [key][d] tile.
+//  * K and V both travel HBM -> LDS with global_load_lds_dwordx4 (no register
+//    staging), double-buffered: block n+1 streams in while block n is
+//    computed.  LDS rows are padded (row + 32 B for d = 128) so that the
+//    operand reads are bank-conflict-free and every operand address is one
+//    base register plus a compile-time offset.
+//  * Softmax in the log2 domain against a fixed per-row reference m: before
+//    the block loop each query row takes the max of its logits over the first
+//    32 keys of its first kept block (the sink block) plus kRefMargin.  The
+//    loop then needs one FMA, one exp2, one add and half a convert per score
+//    and never rescales the AGPR-resident O^T.  m is at most kRefMargin above
+//    the row's true max, so the largest term keeps full precision; a row whose
+//    normaliser reaches 2^kRefOverflow (a logit ~80 nats above the sink chunk)
+//    makes the workgroup recompute the tile with m moved up by log2 of that
+//    normaliser, which bounds every term by 1 (exact, just slower).
+//  * Mean correction: after the kept blocks, the dropped blocks of the row
+//    (the complement of the kept list in [0, i)) are processed 32 at a time
+//    as pseudo-keys: K row = kbar_j, V row = vbar_j (bf16 in LDS), logit bias
+//    log2(n_j), no causal mask (dropped blocks lie strictly before i).
+#include "fp2_device.h"
+#include "fp2_internal.h"
+#include "geometry.h"
+
+namespace fp2 {
+
+constexpr int kRowsPerWave = 64;
+constexpr int kRowsPerPart = 256;
+constexpr int NT = kRowsPerWave / 32;  // 32-query column groups per wave
+constexpr float kRefMargin = 16.0f;     // log2 units above the sink-chunk max
+constexpr float kRefOverflow = 100.0f;  // log2 of the normaliser that forces a rerun
+constexpr int kMaxPasses = 4;
+
+template <int D, int BLK>
+struct Cfg {
+  static constexpr int KS = D / 16;            // k-steps of the QK MFMA along d
+  static constexpr int MT = D / 32;            // 32-row tiles of O^T along d
+  static constexpr int KC = BLK / 32;          // 32-key chunks per block
+  static constexpr int ROWB = D * 2;           // bytes of one bf16 row
+  // LDS row stride: rows are padded so that the 8 rows of a ds_read_b128
+  // phase and the 4 rows of a ds_read_b64_tr_b16 group land on distinct banks.
+  static constexpr int RS = ROWB + (D == 128 ? 32 : 16);
+  static constexpr int TILE = ((BLK * RS + 1023) / 1024) * 1024;  // one K or V tile
+  static constexpr int NLD = TILE / 1024;      // global_load_lds wave ops per tile
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// S^T chunk = sum_ks K_ks Q_ks^T as a chain of v_mfma_f32_32x32x16_bf16 whose
+// accumulator stays in VGPRs (the O^T accumulators own the AGPR file, and the
+// compiler would otherwise place S in AGPRs as well and spill).  Hazards the
+// compiler cannot see through the asm are covered inside it: 2 wait states
+// before the first MFMA (VALU write -> MFMA source read) and 20 after the last
+// (MFMA result -> VALU read); a dependent MFMA chain on the same accumulator
+// needs none.
+__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[8], const bf16x8 (&q)[8]) {
+  f32x16 S;
+  asm("s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %9, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %11, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %5, %13, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %6, %14, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %7, %15, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3"
+      : "=&v"(S)
+      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]),
+        "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
+  return S;
+}
+
+__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[4], const bf16x8 (&q)[4]) {
+  f32x16 S;
+  asm("s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3"
+      : "=&v"(S)
+      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
+  return S;
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_kernel(AttnArgs a) {
+  using C = Cfg<D, BLK>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- tile: KV head fastest (consecutive workgroups of one head share an XCD
+  // under round-robin dispatch), query blocks from the last (longest) down.
+  int t = blockIdx.x;
+  const int h = t % a.Hkv;
+  t /= a.Hkv;
+  const int s = t % a.seq.batch;
+  t /= a.seq.batch;
+  const int part = t % a.parts;
+  t /= a.parts;
+  const int il = a.nqb_grid - 1 - t;
+  const SeqGeo g = seq_geo(a.seq, s, BLK);
+  if (il < 0 || il >= g.nqb) return;
+  const int i = g.first_qb + il;
+  const int G = a.G;
+  const int pr0 = part * kRowsPerPart + wave * kRowsPerWave;
+
+  // query column nt of this lane: packed row pr = pr0 + l32 + 32*nt, i.e.
+  // query head h*G + pr/BLK, row pr%BLK of block i.
+  auto qinfo = [&](int nt, int& rb, long& off) __attribute__((always_inline)) -> bool {
+    const int pr = pr0 + l32 + 32 * nt;
+    const int gq = pr / BLK;
+    rb = pr - gq * BLK;
+    const int r = i * BLK + rb - g.P;
+    off = ((long)(g.qrow0 + r) * a.Hq + (h * G + gq)) * D;
+    return (pr < G * BLK) && r >= 0 && r < g.Sq;
+  };
+  int rib[NT];
+  bf16x8 qop[NT][C::KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    long off;
+    const bool ok = qinfo(nt, rib[nt], off);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ok) {
+        qop[nt][ks] = *(const bf16x8*)((const __bf16*)a.q + off + 16 * ks + 8 * hh);
+      } else {
+        qop[nt][ks] = bf16x8{};
+      }
+    }
+  }
+
+  f32x16 O[C::MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) O[mt][nt] = f32x16{};
+  float mref[NT], lsum[NT];
+
+  // LDS: K tiles at [0, 2*TILE), V tiles at [2*TILE, 4*TILE) (double buffer)
+  char* const lds = smem;
+  const int rowbytes = a.Hkv * C::ROWB;
+  const int Skm1 = g.Sk - 1;
+
+  // K and V tile of key block j -> LDS buffer bb (async, global_load_lds).
+  // Wave op `it` fills tile bytes [1024*it, 1024*it + 1024); lane bytes that
+  // fall into a row pad (or past the last row) reload chunk 0 of a valid row.
+  auto issue_load = [&](int j, int bb) __attribute__((always_inline)) {
+    const int kb0 = j * BLK;
+    for (int it = wave; it < C::NLD; it += nthr >> 6) {
+      const int o = it * 1024 + lane * 16;
+      int row = o / C::RS;
+      const int w = o - row * C::RS;
+      int c = w < C::ROWB ? (w >> 4) : 0;
+      if (row >= BLK) {
+        row = BLK - 1;
+        c = 0;
+      }
+      const int key = min(kb0 + row, Skm1);
+      const char* ks_ = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, key, rowbytes) + h * C::ROWB + c * 16;
+      const char* vs_ = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, key, rowbytes) + h * C::ROWB + c * 16;
+      __builtin_amdgcn_global_load_lds((const void*)ks_, (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vs_, (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024), 16, 0,
+                                       0);
+    }
+  };
+
+  // Per-lane operand base offsets (bytes, within a tile).
+  //  K (A side of S^T): row l32 of the chunk, 16-byte piece 2*ks + hh.
+  //  V (A side of O^T, transpose read): group g = lane/16 reads rows
+  //  K0 + (lane%16)/4 at d = 32*mt + 16*(g%2) + 4*(lane%4), K0 = 16*ks2 +
+  //  8*sec + 4*hh within the chunk.
+  const int koff = l32 * C::RS + hh * 16;
+  const int voff = (4 * hh + ((lane & 15) >> 2)) * C::RS + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+  // K operands of a 32-key chunk (A side of S^T), one 16-byte read per k-step.
+  auto load_kop = [&](const char* kt, int kc, bf16x8 (&kop)[C::KS]) __attribute__((always_inline)) {
+    const char* kb = kt + kc * 32 * C::RS + koff;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) kop[ks] = *(const bf16x8*)(kb + 32 * ks);
+  };
+
+  // One 32-key chunk: S^T = K Q^T, P = exp2(S*scale - m), O^T += V^T P^T.
+  // The chunk's K and V^T operands are read from LDS once and kept in
+  // registers; the query columns of the lane are then processed one after
+  // the other (each is an independent softmax row set).
+  // mode 0: plain; 1: diagonal block (causal mask); 2: pseudo-keys (bias,
+  // slots >= nvalid masked).  Key-in-chunk of accumulator register r:
+  // 8*(r/4) + 4*hh + r%4.
+  auto chunk = [&](const char* kt, const char* vt, int kc, int mode, int nvalid, float bias)
+      __attribute__((always_inline)) {
+    bf16x8 kop[C::KS];
+    load_kop(kt, kc, kop);
+    bf16x8 vop[C::MT][2];
+    const char* vb = vt + kc * 32 * C::RS + voff;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + 16 * ks2 * C::RS));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + (16 * ks2 + 8) * C::RS));
+        vop[mt][ks2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const f32x16 S = qk_chain(kop, qop[nt]);
+      const float mb = mref[nt] - bias;
+      bf16x8 pk[2];
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+        float x = __builtin_fmaf(S[r], a.scale_log2, -mb);
+        if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
+        if (mode == 2 && kic >= nvalid) x = -INFINITY;
+        const float p = __builtin_amdgcn_exp2f(x);
+        sum += p;
+        pk[r >> 3][r & 7] = (__bf16)p;
+      }
+      lsum[nt] += sum;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+          O[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mt][ks2], pk[ks2], O[mt][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- kept blocks (sparse) or all blocks j <= i (dense)
+  const long mrow = ((long)s * a.Hkv + h) * a.seq.nqb_stride + il;
+  const int* list = a.sparse ? a.block_idx + mrow * a.seq.nkb_stride : nullptr;
+  const int nblk = a.sparse ? a.block_cnt[mrow] : i + 1;
+  const int j0 = a.sparse ? list[0] : 0;
+
+  // Reference max per query row: max logit over the first 32 keys of the
+  // first block (causally masked if that block is the diagonal), + margin.
+  issue_load(j0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  {
+    bf16x8 kop[C::KS];
+    load_kop(lds, 0, kop);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const f32x16 S = qk_chain(kop, qop[nt]);
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+        float x = S[r] * a.scale_log2;
+        if (j0 == i && kic > rib[nt]) x = -INFINITY;
+        m = fmaxf(m, x);
+      }
+      m = fmaxf(m, partner32(m));
+      mref[nt] = (m > -INFINITY ? m : 0.f) + kRefMargin;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll 1
+  for (int pass = 0; pass < kMaxPasses; ++pass) {
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[mt][nt] = f32x16{};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lsum[nt] = 0.f;
+    if (pass > 0) {
+      __syncthreads();
+      issue_load(j0, 0);
+    }
+    for (int n = 0; n < nblk; ++n) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (n + 1 < nblk) issue_load(a.sparse ? list[n + 1] : n + 1, (n + 1) & 1);
+      const int j = a.sparse ? list[n] : n;
+      const char* kt = lds + (n & 1) * C::TILE;
+      const char* vt = lds + (2 + (n & 1)) * C::TILE;
+      if (j == i) {
+#pragma unroll 1
+        for (int kc = 0; kc < C::KC; ++kc) chunk(kt, vt, kc, 1, 0, 0.f);
+      } else {
+#pragma unroll 1
+        for (int kc = 0; kc < C::KC; ++kc) chunk(kt, vt, kc, 0, 0, 0.f);
+      }
+    }
+    // ---- mean correction: dropped blocks as pseudo-keys
+    // LDS during this phase: pseudo-K tile (32 rows) | pseudo-V tile (32 rows) |
+    // ndrop | kept-block bitmap | dropped-block list.
+    if (a.sparse && a.mean_correction && i > 0) {
+      __syncthreads();
+      char* pk_t = lds;
+      char* pv_t = lds + 32 * C::RS;
+      int* ndrop_slot = (int*)(lds + 64 * C::RS);
+      uint32_t* bm = (uint32_t*)(ndrop_slot + 1);
+      const int nwords = (i + 31) >> 5;
+      int* drop = (int*)(bm + nwords);
+      for (int w = tid; w < nwords; w += nthr) bm[w] = 0u;
+      __syncthreads();
+      for (int n = tid; n < nblk; n += nthr) {
+        const int j = list[n];
+        if (j < i) atomicOr(&bm[j >> 5], 1u << (j & 31));
+      }
+      __syncthreads();
+      if (wave == 0) {
+        int total = 0;
+        for (int w0 = 0; w0 < nwords; w0 += 64) {
+          const int w = w0 + lane;
+          uint32_t bits = 0u;
+          if (w < nwords) {
+            const uint32_t valid = (w < (i >> 5)) ? 0xffffffffu : ((1u << (i & 31)) - 1u);
+            bits = ~bm[w] & valid;
+          }
+          const int cnt = __popc(bits);
+          const int incl = wave_incl_scan(cnt);
+          int off = total + incl - cnt;
+          while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            drop[off++] = w * 32 + b;
+          }
+          total += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) *ndrop_slot = total;
+      }
+      __syncthreads();
+      const int ndrop = *ndrop_slot;
+      const float* kbr = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
+      const float* vbr = a.vbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
+      const float bias = log2f((float)BLK);  // ln(n_j) in log2 units; dropped blocks are full
+      constexpr int CH8 = D / 8;             // 8-element pieces per row
+      for (int c0 = 0; c0 < ndrop; c0 += 32) {
+        for (int task = tid; task < 2 * 32 * CH8; task += nthr) {
+          const int tensor = task / (32 * CH8);
+          const int rem = task - tensor * 32 * CH8;
+          const int rr = rem / CH8;
+          const int c = rem - rr * CH8;
+          uint4 w = make_uint4(0u, 0u, 0u, 0u);
+          if (c0 + rr < ndrop) {
+            const int id = drop[c0 + rr];
+            const float4* src = (const float4*)((tensor ? vbr : kbr) + (long)id * D + c * 8);
+            const float4 x0 = src[0];
+            const float4 x1 = src[1];
+            w = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                           pack_bf16x2(x1.z, x1.w));
+          }
+          *(uint4*)((tensor ? pv_t : pk_t) + rr * C::RS + c * 16) = w;
+        }
+        __syncthreads();
+        chunk(pk_t, pv_t, 0, 2, min(32, ndrop - c0), bias);
+        __syncthreads();
+      }
+    }
+
+    // A row whose normaliser overflowed the range reruns the tile with its
+    // reference moved up (all rows of the workgroup take part in the rerun;
+    // rows that were fine recompute the same values).
+    bool bad = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float lt = lsum[nt] + partner32(lsum[nt]);
+      if (!(lt < __builtin_exp2f(kRefOverflow))) {
+        bad = true;
+        mref[nt] += (lt < INFINITY) ? log2f(lt) : kRefOverflow;
+      }
+    }
+    if (!__syncthreads_or(bad)) break;
+  }
+
+  // ---- epilogue: O = O^T / l, LSE
+  const bool out32 = a.out_fp32;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int rb;
+    long off;
+    const bool ok = qinfo(nt, rb, off);
+    const float lt = lsum[nt] + partner32(lsum[nt]);
+    const float inv = 1.f / lt;
+    if (ok) {
+      if (a.lse && hh == 0) {
+        const int gq = (pr0 + l32 + 32 * nt) / BLK;
+        const int r = i * BLK + rb - g.P;
+        const long li = a.seq.cu_seqlens_q ? (long)(g.qrow0 + r) * a.Hq + h * G + gq
+                                           : ((long)s * a.Hq + h * G + gq) * a.lse_stride + r;
+        a.lse[li] = (mref[nt] + log2f(lt)) * kLn2;
+      }
+      if (out32) {
+        float* dst = (float*)a.out + off + 4 * hh;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(float4*)(dst + 32 * mt + 8 * q4) =
+                make_float4(O[mt][nt][4 * q4] * inv, O[mt][nt][4 * q4 + 1] * inv, O[mt][nt][4 * q4 + 2] * inv,
+                            O[mt][nt][4 * q4 + 3] * inv);
+      } else {
+        __bf16* dst = (__bf16*)a.out + off + 4 * hh;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(uint2*)(dst + 32 * mt + 8 * q4) =
+                make_uint2(pack_bf16x2(O[mt][nt][4 * q4] * inv, O[mt][nt][4 * q4 + 1] * inv),
+                           pack_bf16x2(O[mt][nt][4 * q4 + 2] * inv, O[mt][nt][4 * q4 + 3] * inv));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// LDS bytes the attention kernel needs for a given key-block count.
+template <int D, int BLK>
+static size_t attn_lds_bytes(int nkb) {
+  using C = Cfg<D, BLK>;
+  size_t lds = 4 * (size_t)C::TILE;
+  const size_t corr = 64 * (size_t)C::RS + 4 + 4 * (size_t)((nkb + 31) / 32) + 4 * (size_t)nkb;
+  return corr > lds ? corr : lds;
+}
+
+template <int D, int BLK>
+static hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
+  const long nwg = (long)a.Hkv * a.seq.batch * a.parts * a.nqb_grid;
+  const size_t lds = attn_lds_bytes<D, BLK>(a.seq.nkb_stride);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_kernel<D, BLK>), dim3((unsigned)nwg), dim3(64 * a.waves), lds, st, a);
+  return hipGetLastError();
+}
+
+size_t attention_lds_bytes(int D, int block, int nkb) {
+  if (D == 128 && block == 128) return attn_lds_bytes<128, 128>(nkb);
+  if (D == 128 && block == 64) return attn_lds_bytes<128, 64>(nkb);
+  if (D == 64 && block == 128) return attn_lds_bytes<64, 128>(nkb);
+  if (D == 64 && block == 64) return attn_lds_bytes<64, 64>(nkb);
+  return 0;
+}
+
+hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t st) {
+  if (fp8) return hipErrorNotSupported;
+  if (D == 128 && block == 128) return launch_t<128, 128>(a, st);
+  if (D == 128 && block == 64) return launch_t<128, 64>(a, st);
+  if (D == 64 && block == 128) return launch_t<64, 128>(a, st);
+  if (D == 64 && block == 64) return launch_t<64, 64>(a, st);
+  return hipErrorNotSupported;
+}
+
+}  // namespace fp2

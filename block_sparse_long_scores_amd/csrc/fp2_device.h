@@ -1,0 +1,70 @@
+// Device-side types and helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp2 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Bit pattern of a bf16 -> fp32 (exact).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Two bf16 packed in a dword -> two floats (exact).
+__device__ __forceinline__ void unpack_bf16x2(uint32_t w, float& lo, float& hi) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xffff0000u);
+}
+
+// fp32 -> bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// OCP e4m3 byte `sel` (0..3) of a dword -> fp32 (v_cvt_f32_fp8; exact).
+__device__ __forceinline__ float fp8_byte_to_f32(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  }
+}
+
+// Wave-wide (64 lanes) reductions through DPP/permute-free shuffles.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Value of the lane 32 apart (v_permlane32_swap): used to combine the two
+// half-waves that hold different keys of the same query column.
+__device__ __forceinline__ float partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0-31: r[0] = own, r[1] = partner; lanes 32-63: r[0] = partner, r[1] = own
+  uint32_t lane = __lane_id();
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+}  // namespace fp2

@@ -1,0 +1,87 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel
+// launchers (*.hip).  Plain structs of device pointers and sizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp2 {
+
+// Geometry of the sequences of one call.  Contiguous calls have `batch`
+// sequences of equal length; paged calls read per-sequence lengths from the
+// device arrays cu_seqlens_q / seqlens_k.
+struct SeqDesc {
+  int batch;          // number of sequences
+  int seqlen_q;       // contiguous: query rows per sequence
+  int seqlen_k;       // contiguous: keys per sequence
+  const int* cu_seqlens_q;  // paged: [batch+1] (device) or nullptr
+  const int* seqlens_k;     // paged: [batch] (device) or nullptr
+  int nqb_stride;     // query blocks per sequence in the mask / qbar arrays
+  int nkb_stride;     // key blocks per sequence in the mask / pooled arrays
+};
+
+// K/V addressing: contiguous [B, Sk, Hkv, D] or paged [pages, page, Hkv, D].
+struct KVDesc {
+  const void* k;
+  const void* v;
+  const int* page_table;    // paged: [batch, max_pages] or nullptr
+  int max_pages;
+  int page_log2;            // log2(page_size) when paged
+};
+
+struct PoolArgs {
+  SeqDesc seq;
+  KVDesc kv;
+  const void* q;            // contiguous [B, Sq, Hq, D] or packed [total_q, Hq, D]
+  float* qbar;              // [B, Hkv, nqb_stride, D]
+  float* kbar;              // [B, Hkv, nkb_stride, D]
+  float* vbar;              // [B, Hkv, nkb_stride, D] or nullptr
+  const float* q_scale;     // fp8 only
+  const float* k_scale;
+  const float* v_scale;
+  int Hq, Hkv, D, block, fp8;
+};
+
+struct SelectArgs {
+  SeqDesc seq;
+  const float* qbar;
+  const float* kbar;
+  int* block_idx;           // [B, Hkv, nqb_stride, nkb_stride]
+  int* block_cnt;           // [B, Hkv, nqb_stride]
+  int Hkv, D, block;
+  float tau;
+  int rows_per_wg;          // query blocks per workgroup
+};
+
+struct AttnArgs {
+  SeqDesc seq;
+  KVDesc kv;
+  const void* q;
+  void* out;
+  float* lse;
+  int lse_stride;           // contiguous: Sq per (b, hq) row; paged layout [total_q, Hq] ignores it
+  const int* block_idx;     // sparse only
+  const int* block_cnt;
+  const float* kbar;        // mean correction only
+  const float* vbar;
+  const float* q_scale;     // fp8 only
+  const float* k_scale;
+  const float* v_scale;
+  int Hq, Hkv, G;
+  float scale_log2;         // softmax_scale * log2(e)
+  int sparse;               // 1: block list + optional correction; 0: dense
+  int mean_correction;
+  int out_fp32;
+  int parts;                // workgroups per (seq, head, q-block) tile
+  int waves;                // waves per workgroup
+  int nqb_grid;             // query-block extent of the grid
+};
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t s);
+// Dynamic LDS bytes of the attention kernel (0 for an unsupported shape).
+size_t attention_lds_bytes(int D, int block, int nkb);
+
+}  // namespace fp2

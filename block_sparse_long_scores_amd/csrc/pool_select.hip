@@ -1,0 +1,266 @@
+// Pattern discovery and max-based dynamic thresholding on gfx950.
+//
+// Source: "FlashPrefill V2: block-sparse prefill attention for long-context LLM
+// serving", abstract (instantaneous pattern discovery, max-based dynamic
+// thresholding, mean correction), and the papers.ananclaw.com explainer §2.1
+// (Supp(q), the dropped blocks' average value).  Pattern discovery is read as
+// block mean-pooling with unscaled pooled-Q . pooled-K block scores; a key
+// block is kept when its score is at least the row maximum minus tau, and the
+// sink block 0 and the diagonal block are always kept.
+//
+// pool_kernel   : one workgroup per query block (all KV groups at once) or
+//                 per key block (K and V at once).  Streams the rows once from
+//                 HBM with 16-byte coalesced loads, accumulates in fp32.
+// select_kernel : one workgroup per (sequence, KV head, run of query blocks).
+//                 Scores every visible key block against the run's pooled
+//                 queries, reduces each row's maximum across the wavefront and
+//                 compacts the kept blocks into an ascending index list with
+//                 a ballot prefix count.
+#include "fp2_device.h"
+#include "fp2_internal.h"
+#include "geometry.h"
+
+namespace fp2 {
+
+constexpr int kPoolThreads = 256;
+constexpr int kMaxChunksPerThread = 4;
+
+// Accumulate one 16-byte chunk of a row into acc[EPC] (fp32).
+template <int ESZ>
+__device__ __forceinline__ void acc_chunk(float* acc, const uint4& w) {
+  if constexpr (ESZ == 2) {
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float lo, hi;
+      unpack_bf16x2(ws[e], lo, hi);
+      acc[2 * e] += lo;
+      acc[2 * e + 1] += hi;
+    }
+  } else {
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[4 * e + b] += fp8_byte_to_f32(ws[e], b);
+    }
+  }
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
+  constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
+  extern __shared__ float red[];
+  const int s = blockIdx.y;
+  const SeqGeo g = seq_geo(a.seq, s, a.block);
+  const int t = threadIdx.x;
+  const int x = blockIdx.x;
+  const int D = a.D;
+
+  if (x < a.seq.nqb_stride) {
+    // ---- query block: mean over the G heads of each group and the rows present
+    const int il = x;
+    if (il >= g.nqb) return;
+    const int i = g.first_qb + il;
+    const int r0 = max(i * a.block, g.P) - g.P;
+    const int r1 = min((i + 1) * a.block, g.Sk) - g.P;
+    const int W = a.Hq * D;
+    const int nch = W / EPC;
+    const char* base = (const char*)a.q + (long)(g.qrow0 + r0) * W * ESZ;
+    float acc[kMaxChunksPerThread][EPC];
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
+    const int nr = r1 - r0;
+    int r = 0;
+    for (; r + 4 <= nr; r += 4) {
+      uint4 w[4][kMaxChunksPerThread];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < kMaxChunksPerThread; ++c) {
+          int ch = t + c * kPoolThreads;
+          if (ch < nch) w[u][c] = *(const uint4*)(base + (long)(r + u) * W * ESZ + ch * 16);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < kMaxChunksPerThread; ++c)
+          if (t + c * kPoolThreads < nch) acc_chunk<ESZ>(acc[c], w[u][c]);
+    }
+    for (; r < nr; ++r) {
+#pragma unroll
+      for (int c = 0; c < kMaxChunksPerThread; ++c) {
+        int ch = t + c * kPoolThreads;
+        if (ch < nch) acc_chunk<ESZ>(acc[c], *(const uint4*)(base + (long)r * W * ESZ + ch * 16));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      int ch = t + c * kPoolThreads;
+      if (ch < nch) {
+        int e0 = ch * EPC;
+        float sc = (ESZ == 1) ? a.q_scale[e0 / D] : 1.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) red[e0 + e] = acc[c][e] * sc;
+      }
+    }
+    __syncthreads();
+    const int G = a.Hq / a.Hkv;
+    const float inv = 1.f / (float)(G * nr);
+    for (int o = t; o < a.Hkv * D; o += kPoolThreads) {
+      int h = o / D, dd = o - h * D;
+      float sum = 0.f;
+      for (int gg = 0; gg < G; ++gg) sum += red[(h * G + gg) * D + dd];
+      a.qbar[(((long)s * a.Hkv + h) * a.seq.nqb_stride + il) * D + dd] = sum * inv;
+    }
+    return;
+  }
+
+  // ---- key block: means of K and V over the keys of block j
+  const int j = x - a.seq.nqb_stride;
+  if (j >= g.nkb) return;
+  const int c0 = j * a.block;
+  const int c1 = min(c0 + a.block, g.Sk);
+  const int W = a.Hkv * D;
+  const int nch = W / EPC;
+  const int ntask = a.vbar ? 2 * nch : nch;
+  const int rowbytes = W * ESZ;
+  float acc[kMaxChunksPerThread][EPC];
+#pragma unroll
+  for (int c = 0; c < kMaxChunksPerThread; ++c)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
+  for (int cc = c0; cc < c1; ++cc) {
+    const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc, rowbytes);
+    const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc, rowbytes);
+    uint4 w[kMaxChunksPerThread];
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      int task = t + c * kPoolThreads;
+      if (task < ntask) {
+        const char* row = task < nch ? krow : vrow;
+        int ch = task < nch ? task : task - nch;
+        w[c] = *(const uint4*)(row + ch * 16);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c)
+      if (t + c * kPoolThreads < ntask) acc_chunk<ESZ>(acc[c], w[c]);
+  }
+  const float inv = 1.f / (float)(c1 - c0);
+#pragma unroll
+  for (int c = 0; c < kMaxChunksPerThread; ++c) {
+    int task = t + c * kPoolThreads;
+    if (task < ntask) {
+      bool isv = task >= nch;
+      int ch = isv ? task - nch : task;
+      int e0 = ch * EPC;
+      int h = e0 / D, dd = e0 - h * D;
+      float sc = inv;
+      if (ESZ == 1) sc *= (isv ? a.v_scale : a.k_scale)[h];
+      float* dst = (isv ? a.vbar : a.kbar) + (((long)s * a.Hkv + h) * a.seq.nkb_stride + j) * D + dd;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) dst[e] = acc[c][e] * sc;
+    }
+  }
+}
+
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
+  extern __shared__ float smem[];
+  const int s = blockIdx.z;
+  const int h = blockIdx.y;
+  const SeqGeo g = seq_geo(a.seq, s, a.block);
+  const int TQ = a.rows_per_wg;
+  const int il0 = blockIdx.x * TQ;
+  if (il0 >= g.nqb) return;
+  const int nrows = min(TQ, g.nqb - il0);
+  const int D = a.D;
+  const int jmax = g.first_qb + il0 + nrows - 1;  // last visible key block of the run
+  const int ncols = jmax + 1;
+  float* qb = smem;                 // [TQ][D]
+  float* sc = smem + TQ * D;        // [TQ][ncols]
+  const int t = threadIdx.x;
+  const float* qsrc = a.qbar + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il0) * D;
+  for (int o = t; o < nrows * D; o += kSelThreads) qb[o] = qsrc[o];
+  __syncthreads();
+
+  // scores S[r][j] = <qbar_r, kbar_j> for all j <= jmax (fp32, fixed fma order)
+  const float* kb = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
+  for (int j = t; j < ncols; j += kSelThreads) {
+    float acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const float4* krow = (const float4*)(kb + (long)j * D);
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      float4 kv = krow[d4];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (r < nrows) {
+          float4 qv = *(const float4*)(qb + r * D + 4 * d4);
+          acc[r] = fmaf(qv.x, kv.x, acc[r]);
+          acc[r] = fmaf(qv.y, kv.y, acc[r]);
+          acc[r] = fmaf(qv.z, kv.z, acc[r]);
+          acc[r] = fmaf(qv.w, kv.w, acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r < nrows) sc[r * ncols + j] = acc[r];
+  }
+  __syncthreads();
+
+  // per row: max over j <= i, threshold, ascending compaction
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = wave; r < nrows; r += kSelThreads / 64) {
+    const int il = il0 + r;
+    const int i = g.first_qb + il;
+    const float* row = sc + r * ncols;
+    float m = -INFINITY;
+    for (int j = lane; j <= i; j += 64) m = fmaxf(m, row[j]);
+    m = wave_max(m);
+    const float thr = m - a.tau;
+    int* dst = a.block_idx + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il) * (long)a.seq.nkb_stride;
+    int base = 0;
+    for (int j0 = 0; j0 <= i; j0 += 64) {
+      int j = j0 + lane;
+      bool keep = false;
+      if (j <= i) keep = (row[j] >= thr) || j == 0 || j == i;
+      uint64_t mask = __ballot(keep);
+      if (keep) dst[base + __popcll(mask & lt_mask)] = j;
+      base += __popcll(mask);
+    }
+    if (lane == 0) a.block_cnt[((long)s * a.Hkv + h) * a.seq.nqb_stride + il] = base;
+  }
+}
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
+  dim3 grid(a.seq.nqb_stride + a.seq.nkb_stride, a.seq.batch);
+  size_t lds = (size_t)a.Hq * a.D * sizeof(float);
+  if (a.fp8) {
+    hipLaunchKernelGGL(pool_kernel<1>, grid, dim3(kPoolThreads), lds, st, a);
+  } else {
+    hipLaunchKernelGGL(pool_kernel<2>, grid, dim3(kPoolThreads), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
+  dim3 grid((a.seq.nqb_stride + a.rows_per_wg - 1) / a.rows_per_wg, a.Hkv, a.seq.batch);
+  size_t lds = (size_t)a.rows_per_wg * (a.D + a.seq.nkb_stride) * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fp2

@@ -1,0 +1,193 @@
+/*
+ * fp2.h -- C ABI of the MI355X (gfx950) block-sparse causal prefill attention
+ * library: block selection, sparse attention with mean correction, the dense
+ * causal baseline, and the paged-KV / chunked-prefill path.
+ *
+ * The operation (sources are cited by page title and section):
+ *  - "FlashPrefill V2: block-sparse prefill attention for long-context LLM
+ *    serving", abstract: instantaneous pattern discovery and max-based dynamic
+ *    thresholding select the key blocks each query block attends to; a mean
+ *    correction term suppresses the error of the dropped blocks; the operator
+ *    supports GQA (PackGQA), FP8, paged KV cache and continuous batching.
+ *  - papers.ananclaw.com explainer, §2.1: for query block q only the
+ *    threshold-selected keys Supp(q) are computed; V2 adds the mean
+ *    correction Out_q^V2 built from mu_q and the dropped blocks' average value.
+ *    §2.2: PackGQA (the query heads of one GQA group share a K/V tile).
+ *    §2.3: FP8 E4M3 with scale calibration; paged KV whose block size matches
+ *    the page table; continuous batching.
+ *
+ * What the library computes, per sequence, KV head h and query block i
+ * (blocks numbered by absolute position, block size b):
+ *  1. qbar_i = mean of Q over the G = Hq/Hkv query heads of group h and the
+ *     rows of block i present in the call; kbar_j, vbar_j = means of K, V over
+ *     the keys of block j (fp32 accumulation).
+ *  2. S_ij = <qbar_i, kbar_j> (unscaled), 0 <= j <= i; m_i = max_j S_ij;
+ *     block j is kept iff S_ij >= m_i - tau; blocks 0 and i are always kept.
+ *  3. Each query row attends causally to the keys of the kept blocks.
+ *  4. With mean_correction != 0 every dropped block j enters the same softmax
+ *     as one pseudo-key with logit softmax_scale*<q, kbar_j> + ln(n_j) and
+ *     value vbar_j (n_j = keys in block j).
+ *  5. out = normalised sum; lse = natural log of the softmax denominator.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers, scalars and the params struct are
+ *    host memory.  The caller owns every buffer, the workspace included; the
+ *    library allocates no device memory and keeps no pointer after a call.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Buffers must stay valid until the stream has run it.
+ *  - Layouts are row-major.  Contiguous tensors are BSHD: q [B, Sq, Hq, d],
+ *    k and v [B, Sk, Hkv, d], out [B, Sq, Hq, d].  Query head hq reads KV
+ *    head hq / G.  Query row r of a sequence sits at absolute position
+ *    Sk - Sq + r (Sq < Sk is a chunked prefill over a cached prefix).
+ *  - Host-side validation runs before anything is enqueued; on any error the
+ *    call returns a negative fp2_status, enqueues nothing, and
+ *    fp2_last_error() (thread-local) describes the problem.  A failed launch
+ *    returns FP2_EDEVICE.  No C++ exception crosses this interface.
+ *  - Supported shapes: head_dim in {64, 128}; block_size in {64, 128};
+ *    num_q_heads a positive multiple of num_kv_heads; in_dtype FP2_BF16 or
+ *    FP2_FP8_E4M3; out_dtype FP2_BF16 or FP2_FP32.
+ */
+#ifndef FP2_H
+#define FP2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP2_OK = 0,
+  FP2_EINVAL = -1,        /* bad argument (null pointer, bad size, NaN tau) */
+  FP2_EUNSUPPORTED = -2,  /* valid request outside the supported shapes     */
+  FP2_EWORKSPACE = -3,    /* workspace missing or smaller than required     */
+  FP2_EDEVICE = -4        /* HIP runtime or launch error                    */
+} fp2_status;
+
+typedef enum { FP2_BF16 = 0, FP2_FP8_E4M3 = 1, FP2_FP32 = 2 } fp2_dtype;
+
+typedef struct {
+  int32_t num_q_heads;     /* Hq                                               */
+  int32_t num_kv_heads;    /* Hkv; G = Hq / Hkv                                */
+  int32_t head_dim;        /* d: 64 or 128                                     */
+  int32_t block_size;      /* b: 64 or 128 (the selection granularity)         */
+  float softmax_scale;     /* <= 0 means 1/sqrt(head_dim)                      */
+  float tau;               /* threshold; +INFINITY keeps every block; NaN is an error */
+  int32_t mean_correction; /* 0: drop blocks outright; 1: pseudo-key correction */
+  int32_t in_dtype;        /* fp2_dtype of q, k, v: FP2_BF16 or FP2_FP8_E4M3   */
+  int32_t out_dtype;       /* fp2_dtype of out: FP2_BF16 or FP2_FP32           */
+  /* FP8 only (E4M3, OCP "e4m3fn" encoding): per-head dequantization scales,
+   * DEVICE fp32 arrays q_scale [Hq], k_scale [Hkv], v_scale [Hkv]; a value is
+   * code * scale.  Ignored for bf16 inputs.                                   */
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+} fp2_params;
+
+/* Number of query blocks a sequence touches: blocks of absolute positions
+ * [Sk - Sq, Sk), i.e. (Sk-1)/b - (Sk-Sq)/b + 1.  Key blocks: ceil(Sk / b). */
+int32_t fp2_num_q_blocks(int32_t seqlen_q, int32_t seqlen_k, int32_t block_size);
+int32_t fp2_num_k_blocks(int32_t seqlen_k, int32_t block_size);
+
+/* Workspace bytes needed by fp2_select_blocks for this problem size (the
+ * pooled query blocks, fp32).  Returns 0 for invalid parameters.             */
+size_t fp2_select_workspace_size(const fp2_params* p, int32_t batch,
+                                 int32_t seqlen_q, int32_t seqlen_k);
+
+/* Block selection (steps 1-2 above; abstract: pattern discovery and max-based
+ * dynamic thresholding; explainer §2.1: Supp(q)).
+ *   q, k, v    : contiguous BSHD inputs (in_dtype).
+ *   block_idx  : int32 [B, Hkv, nqb, nkb]; row (b, h, il) receives the kept
+ *                key blocks of query block il (local index; absolute block
+ *                (Sk-Sq)/b + il) in ascending order in entries [0, cnt);
+ *                entries [cnt, nkb) are left undefined.
+ *   block_cnt  : int32 [B, Hkv, nqb], the number of kept blocks per row.
+ *   pooled_k   : fp32 [B, Hkv, nkb, d], the key-block means kbar.
+ *   pooled_v   : fp32 [B, Hkv, nkb, d], the value-block means vbar; may be
+ *                NULL (then not written).
+ *   workspace  : device scratch of at least fp2_select_workspace_size bytes. */
+fp2_status fp2_select_blocks(const fp2_params* p, int32_t batch,
+                             int32_t seqlen_q, int32_t seqlen_k,
+                             const void* q, const void* k, const void* v,
+                             int32_t* block_idx, int32_t* block_cnt,
+                             float* pooled_k, float* pooled_v,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Block-sparse causal attention with mean correction (steps 3-5; explainer
+ * §2.1 Out_q^V2, §2.2 PackGQA).  Takes the mask and pooled blocks in the
+ * layout fp2_select_blocks produces.  Any mask is accepted whose rows are
+ * strictly ascending lists of blocks in [0, i] that contain the diagonal
+ * block i; the dropped set of a row is the complement of its list in [0, i].
+ * pooled_k and pooled_v are read only when mean_correction != 0 (then both
+ * must be non-NULL).
+ *   out : [B, Sq, Hq, d] in out_dtype.   lse : fp32 [B, Hq, Sq] or NULL.    */
+fp2_status fp2_sparse_prefill(const fp2_params* p, int32_t batch,
+                              int32_t seqlen_q, int32_t seqlen_k,
+                              const void* q, const void* k, const void* v,
+                              const int32_t* block_idx, const int32_t* block_cnt,
+                              const float* pooled_k, const float* pooled_v,
+                              void* out, float* lse, void* stream);
+
+/* Dense causal attention softmax(scale * Q K^T) V over every key up to the
+ * query's position (explainer §1.1; the abstract's dense baseline): the same
+ * kernel as fp2_sparse_prefill with every block kept and no correction.
+ * tau and mean_correction are ignored.                                       */
+fp2_status fp2_dense_prefill(const fp2_params* p, int32_t batch,
+                             int32_t seqlen_q, int32_t seqlen_k,
+                             const void* q, const void* k, const void* v,
+                             void* out, float* lse, void* stream);
+
+/* Paged KV cache + continuous batch (abstract: paged KV cache and continuous
+ * batching; explainer §2.3: KV block size matches the page table).
+ *   q            : [total_q, Hq, d] packed new query rows of all sequences.
+ *   cu_seqlens_q : int32 [num_seqs + 1] device, row offsets into q (and out).
+ *   seqlens_k    : int32 [num_seqs] device, tokens in the cache per sequence,
+ *                  the new chunk included (its K/V must already be written).
+ *                  Sequence s has q_len = cu[s+1] - cu[s] <= seqlens_k[s]; its
+ *                  query row r sits at position seqlens_k[s] - q_len + r.
+ *   max_seqlen_q, max_seqlen_k : host upper bounds of q_len and seqlens_k.
+ *   k_cache, v_cache : [num_pages, page_size, Hkv, d] (in_dtype).
+ *   page_size    : must divide block_size.
+ *   page_table   : int32 [num_seqs, max_pages_per_seq] device; token t of
+ *                  sequence s lives in page page_table[s][t / page_size], row
+ *                  t % page_size.  Entries must be in [0, num_pages); with
+ *                  FP2_VALIDATE=1 in the environment the call copies the
+ *                  lengths and the table to the host (synchronising the
+ *                  stream) and rejects out-of-range values, otherwise they
+ *                  are undefined behaviour.
+ *   out          : [total_q, Hq, d] out_dtype.  lse: fp32 [total_q, Hq] or NULL.
+ *   block_idx, block_cnt : optional mask export (both NULL or both set), laid
+ *                  out [num_seqs, Hkv, max_nqb, max_nkb] and
+ *                  [num_seqs, Hkv, max_nqb] with the sizes given by
+ *                  fp2_paged_mask_dims; row il of sequence s is its il-th
+ *                  query block, as in fp2_select_blocks.
+ *   workspace    : at least fp2_paged_workspace_size bytes.                 */
+void fp2_paged_mask_dims(const fp2_params* p, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, int32_t* max_nqb, int32_t* max_nkb);
+size_t fp2_paged_workspace_size(const fp2_params* p, int32_t num_seqs,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k);
+fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs,
+                                    const void* q, const int32_t* cu_seqlens_q,
+                                    const int32_t* seqlens_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    const void* k_cache, const void* v_cache,
+                                    int32_t num_pages, int32_t page_size,
+                                    const int32_t* page_table, int32_t max_pages_per_seq,
+                                    void* out, float* lse,
+                                    int32_t* block_idx, int32_t* block_cnt,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* fp2_status_string(fp2_status s);
+/* Description of the last error raised on the calling thread ("" if none). */
+const char* fp2_last_error(void);
+/* Library version string. */
+const char* fp2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP2_H */

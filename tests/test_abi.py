@@ -1,0 +1,111 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/fp2.h declares, and host-side validation rejects bad
+arguments with the documented status before anything is enqueued."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_long_scores_amd as fp2
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp2.h")
+
+FAKE = 0x1000  # non-NULL pointer that is never dereferenced by validation
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp2_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fp2.load()
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in fp2.EXPORTED, n
+    assert fp2.fp2_version().startswith("fp2")
+
+
+def params(**kw):
+    d = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=128, tau=1.0)
+    d.update(kw)
+    return fp2.make_params(d["num_q_heads"], d["num_kv_heads"], d["head_dim"], d["block_size"], tau=d["tau"])
+
+
+def select(p, batch=1, sq=1024, sk=1024, ws=1 << 30, q=FAKE, wsp=FAKE):
+    return fp2.fp2_select_blocks(p, batch, sq, sk, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsp, ws, None)
+
+
+def test_block_counts():
+    assert fp2.fp2_num_q_blocks(1024, 1024, 128) == 8
+    assert fp2.fp2_num_q_blocks(100, 1000, 128) == 1      # positions 900..999
+    assert fp2.fp2_num_q_blocks(200, 1000, 128) == 2      # 800..999 spans blocks 6, 7
+    assert fp2.fp2_num_k_blocks(1000, 128) == 8
+    assert fp2.fp2_num_q_blocks(10, 5, 128) == 0
+
+
+def test_workspace_sizes():
+    p = params()
+    assert fp2.fp2_select_workspace_size(p, 1, 1024, 1024) == 2 * 8 * 128 * 4
+    assert fp2.fp2_select_workspace_size(params(head_dim=96), 1, 1024, 1024) == 0
+    mq, mk = fp2.fp2_paged_mask_dims(p, 16384, 131072)
+    assert (mq, mk) == (129, 1024)
+    assert fp2.fp2_paged_workspace_size(p, 6, 32768, 131072) > 0
+
+
+def test_validation_errors():
+    lib = fp2.load()
+    assert lib.fp2_select_blocks(None, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == fp2.FP2_EINVAL
+    assert "params" in fp2.last_error()
+    assert select(params(num_q_heads=6, num_kv_heads=4)) == fp2.FP2_EINVAL
+    assert select(params(head_dim=96)) == fp2.FP2_EUNSUPPORTED
+    assert select(params(block_size=32)) == fp2.FP2_EUNSUPPORTED
+    assert select(params(tau=float("nan"))) == fp2.FP2_EINVAL
+    assert select(params(), batch=0) == fp2.FP2_EINVAL
+    assert select(params(), sq=2048, sk=1024) == fp2.FP2_EINVAL
+    assert select(params(), q=None) == fp2.FP2_EINVAL
+    assert select(params(), ws=16) == fp2.FP2_EWORKSPACE
+    assert select(params(), wsp=None) == fp2.FP2_EWORKSPACE
+    assert "workspace" in fp2.last_error()
+    p = params()
+    p.in_dtype = fp2.FP2_FP8_E4M3
+    assert select(p) == fp2.FP2_EINVAL                      # fp8 without scales
+    p = params()
+    p.out_dtype = 7
+    assert fp2.fp2_dense_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == fp2.FP2_EUNSUPPORTED
+    p = params()
+    p.mean_correction = 1
+    assert fp2.fp2_sparse_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                  None) == fp2.FP2_EINVAL   # correction needs pooled blocks
+
+
+def test_paged_validation_errors():
+    p = params()
+    args = dict(q=FAKE, cu=FAKE, sk=FAKE, mq=1024, mk=4096, kc=FAKE, vc=FAKE, npages=64, page=64, table=FAKE,
+                mpp=64, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return fp2.fp2_sparse_prefill_paged(p, 2, a["q"], a["cu"], a["sk"], a["mq"], a["mk"], a["kc"], a["vc"],
+                                            a["npages"], a["page"], a["table"], a["mpp"], a["out"], a["lse"],
+                                            a["idx"], a["cnt"], a["ws"], a["wsb"], None)
+    assert call(page=48) == fp2.FP2_EUNSUPPORTED
+    assert call(page=256) == fp2.FP2_EUNSUPPORTED           # must divide the block size
+    assert call(table=None) == fp2.FP2_EINVAL
+    assert call(idx=FAKE) == fp2.FP2_EINVAL                 # idx without cnt
+    assert call(mpp=8) == fp2.FP2_EINVAL                    # table too short for max_seqlen_k
+    assert call(wsb=1024) == fp2.FP2_EWORKSPACE
+    assert call(npages=0) == fp2.FP2_EINVAL
+
+
+def test_status_strings():
+    assert fp2.status_string(fp2.FP2_OK) == "FP2_OK"
+    assert fp2.status_string(fp2.FP2_EWORKSPACE) == "FP2_EWORKSPACE"
+    assert fp2.status_string(-99) == "FP2_UNKNOWN"
