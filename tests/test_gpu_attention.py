@@ -80,7 +80,7 @@ def test_tiny_all_kept_fp32_out(gpu):
     ref = A.sparse_prefill(qn, kn, vn, hkv, b, 2.0)
     kept_gpu = kept_from_lists(idx[0], cnt[0], ref["geo"].nkb)
     assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
-    o = f64(out[0])
+    o = f64(out).reshape(ref["O"].shape)
     e = rel_l2(o, ref["O"])
     print(f"[tiny] rel_l2={e:.2e} max_abs={max_abs(o, ref['O']):.2e}", flush=True)
     assert e < BF16_REL_L2
@@ -101,7 +101,7 @@ def test_sparse_attention_matches_oracle(gpu, S, Sq, target):
     kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
     qbar, kbar, vbar, n_k = A.pool(qn, kn, vn, hkv, b)
     O, L = A.attend(qn, kn, vn, kept_gpu, kbar, vbar, n_k, hkv, b, 1 / math.sqrt(d), True)
-    o = f64(out[0])
+    o = f64(out).reshape(O.shape)
     e, m = rel_l2(o, O), max_abs(o, O)
     print(f"[sparse] tau={tau:.3f} sparsity={A.sparsity(kept_gpu, geo.q_block_ids()):.3f} rel_l2={e:.2e} max_abs={m:.2e}",
           flush=True)
@@ -118,7 +118,7 @@ def test_dense_matches_textbook(gpu, S, Sq):
     out, lse = gpu.dense_prefill(p, q, k, v, return_lse=True)
     torch.cuda.synchronize()
     O, L = A.dense_attention(f64(pr.q), f64(pr.k), f64(pr.v), hkv, 1 / math.sqrt(d))
-    o = f64(out[0])
+    o = f64(out).reshape(O.shape)
     e, m = rel_l2(o, O), max_abs(o, O)
     print(f"[dense] rel_l2={e:.2e} max_abs={m:.2e}", flush=True)
     assert e < BF16_REL_L2 and m < BF16_MAX_ABS
@@ -161,7 +161,8 @@ def test_gqa_wider_group_and_small_blocks(gpu):
         kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
         qbar, kbar, vbar, n_k = A.pool(qn, kn, vn, hkv, b)
         O, _ = A.attend(qn, kn, vn, kept_gpu, kbar, vbar, n_k, hkv, b, 1 / math.sqrt(d), True)
-        e, m = rel_l2(f64(out[0]), O), max_abs(f64(out[0]), O)
+        o = f64(out).reshape(O.shape)
+        e, m = rel_l2(o, O), max_abs(o, O)
         print(f"[gqa] hq={hq} hkv={hkv} d={d} b={b} rel_l2={e:.2e} max_abs={m:.2e}", flush=True)
         assert e < BF16_REL_L2 and m < BF16_MAX_ABS
 
@@ -179,4 +180,4 @@ def test_batch2_matches_per_sequence(gpu):
         i1, c1, k1, v1 = gpu.select_blocks(p, q[s], k[s], v[s])
         o1 = gpu.sparse_prefill(p, q[s], k[s], v[s], i1, c1, k1, v1)
         torch.cuda.synchronize()
-        assert torch.equal(c1[0], cnt[s]) and torch.equal(o1[0], out[s])
+        assert torch.equal(c1[0], cnt[s]) and torch.equal(o1, out[s])

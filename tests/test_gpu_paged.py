@@ -48,4 +48,4 @@ def test_paged_matches_oracle_and_contiguous(gpu):
         o2 = gpu.sparse_prefill(p, qc, kc, vc, i2, c2, pk2, pv2)
         torch.cuda.synchronize()
         assert torch.equal(c2[0], cnt[s, :, :geo.nqb])
-        assert torch.equal(o2[0], out[cu[s]:cu[s + 1]])
+        assert torch.equal(o2, out[cu[s]:cu[s + 1]])
