@@ -64,7 +64,16 @@ struct Cfg {
   static constexpr int RS = ROWB + (D == 128 ? 32 : 16);
   static constexpr int TILE = ((BLK * RS + 1023) / 1024) * 1024;  // one K or V tile
   static constexpr int NLD = TILE / 1024;      // global_load_lds wave ops per tile
+  static constexpr int PSB = 32 * RS;          // one 32-row pseudo-key tile (bf16)
+  static constexpr int STG = 2 * 32 * D * 4;   // fp32 kbar + vbar rows of one pseudo chunk
 };
+
+// Byte offset of the correction-phase staging buffers (after the pseudo tiles,
+// the count, the bitmap and the dropped list).
+template <int D, int BLK>
+__host__ __device__ constexpr int corr_stage_offset(int nkb) {
+  return ((2 * Cfg<D, BLK>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb + 1023) / 1024) * 1024;
+}
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = __lane_id();
@@ -128,16 +137,20 @@ void attn_kernel(AttnArgs a) {
   const int hh = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- tile: KV head fastest (consecutive workgroups of one head share an XCD
-  // under round-robin dispatch), query blocks from the last (longest) down.
-  int t = blockIdx.x;
+  // ---- tile.  Query blocks go from the last (longest) down; the G2 =
+  // Hkv*batch*parts tiles of one query block are rotated by the query-block
+  // rank, so that under the round-robin workgroup -> XCD dispatch each XCD
+  // serves every head in turn (kept-block counts differ between heads) while
+  // the parts of one tile stay on the same XCD.
+  const int G2 = a.Hkv * a.seq.batch * a.parts;
+  const int rank = blockIdx.x / G2;
+  int t = (blockIdx.x - rank * G2 + rank) % G2;
   const int h = t % a.Hkv;
   t /= a.Hkv;
   const int s = t % a.seq.batch;
   t /= a.seq.batch;
-  const int part = t % a.parts;
-  t /= a.parts;
-  const int il = a.nqb_grid - 1 - t;
+  const int part = t;
+  const int il = a.nqb_grid - 1 - rank;
   const SeqGeo g = seq_geo(a.seq, s, BLK);
   if (il < 0 || il >= g.nqb) return;
   const int i = g.first_qb + il;
@@ -219,19 +232,8 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) kop[ks] = *(const bf16x8*)(kb + 32 * ks);
   };
-
-  // One 32-key chunk: S^T = K Q^T, P = exp2(S*scale - m), O^T += V^T P^T.
-  // The chunk's K and V^T operands are read from LDS once and kept in
-  // registers; the query columns of the lane are then processed one after
-  // the other (each is an independent softmax row set).
-  // mode 0: plain; 1: diagonal block (causal mask); 2: pseudo-keys (bias,
-  // slots >= nvalid masked).  Key-in-chunk of accumulator register r:
-  // 8*(r/4) + 4*hh + r%4.
-  auto chunk = [&](const char* kt, const char* vt, int kc, int mode, int nvalid, float bias)
-      __attribute__((always_inline)) {
-    bf16x8 kop[C::KS];
-    load_kop(kt, kc, kop);
-    bf16x8 vop[C::MT][2];
+  // V^T operands of a 32-key chunk (A side of O^T), two transpose reads each.
+  auto load_vop = [&](const char* vt, int kc, bf16x8 (&vop)[C::MT][2]) __attribute__((always_inline)) {
     const char* vb = vt + kc * 32 * C::RS + voff;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
@@ -244,30 +246,99 @@ void attn_kernel(AttnArgs a) {
         vop[mt][ks2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
+  };
+  auto qk = [&](const bf16x8 (&kop)[C::KS], int nt) __attribute__((always_inline)) -> f32x16 {
+    f32x16 S = f32x16{};
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const f32x16 S = qk_chain(kop, qop[nt]);
-      const float mb = mref[nt] - bias;
-      bf16x8 pk[2];
-      float sum = 0.f;
+    for (int ks = 0; ks < C::KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[nt][ks], S, 0, 0, 0);
+    return S;
+  };
+  // P = exp2(S*scale - m + bias) as bf16 B-operands, row sums into lsum.
+  // mode 0: plain; 1: diagonal block (causal mask); 2: pseudo-keys (slots >=
+  // nvalid masked).  Key-in-chunk of accumulator register r: 8*(r/4) + 4*hh + r%4.
+  auto softmax = [&](const f32x16& S, int nt, int kc, int mode, int nvalid, float bias, bf16x8 (&pk)[2])
+      __attribute__((always_inline)) {
+    const float mb = mref[nt] - bias;
+    float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-        float x = __builtin_fmaf(S[r], a.scale_log2, -mb);
-        if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
-        if (mode == 2 && kic >= nvalid) x = -INFINITY;
-        const float p = __builtin_amdgcn_exp2f(x);
-        sum += p;
-        pk[r >> 3][r & 7] = (__bf16)p;
-      }
-      lsum[nt] += sum;
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2)
-          O[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mt][ks2], pk[ks2], O[mt][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int r = 0; r < 16; ++r) {
+      const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+      float x = __builtin_fmaf(S[r], a.scale_log2, -mb);
+      if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
+      if (mode == 2 && kic >= nvalid) x = -INFINITY;
+      const float p = __builtin_amdgcn_exp2f(x);
+      sum += p;
+      pk[r >> 3][r & 7] = (__bf16)p;
     }
+    lsum[nt] += sum;
+  };
+  auto pv = [&](const bf16x8 (&vop)[C::MT][2], const bf16x8 (&pk)[2], int nt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+        O[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mt][ks2], pk[ks2], O[mt][nt], 0, 0, 0);
+  };
+
+  // Interleave hint for one pipeline stage: nmfma MFMAs, each followed by a
+  // slice of the stage's VALU work (the softmax of the other column set).
+  auto interleave = [&](int nmfma) __attribute__((always_inline)) {
+    for (int k = 0; k < nmfma; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+  };
+
+  // The NCH 32-key chunks of one K/V tile (or of one pseudo-key tile),
+  // software-pipelined in two stages per chunk c:
+  //   stage 1: softmax(S_c, columns 0)  ||  QK(c+1, columns 0), PV(c-1, columns 1)
+  //   stage 2: softmax(S_c, columns 1)  ||  QK(c+1, columns 1), PV(c, columns 0)
+  // so the exp/sum/convert VALU work of one column set runs under the MFMAs of
+  // the other; PV(last, columns 1) closes the tile.
+  auto run_tile = [&](const char* kt, const char* vt, int nch, int mode, int nvalid, float bias)
+      __attribute__((always_inline)) {
+    bf16x8 kop[C::KS];
+    bf16x8 vop_c[C::MT][2], vop_p[C::MT][2];
+    bf16x8 p0[2], p1[2];
+    load_kop(kt, 0, kop);
+    load_vop(vt, 0, vop_c);
+    f32x16 S0 = qk(kop, 0);
+    f32x16 S1 = qk(kop, 1);
+#pragma unroll
+    for (int c = 0; c < C::KC; ++c) {
+      if (c >= nch) break;
+      const bool more = c + 1 < nch;
+      if (more) load_kop(kt, c + 1, kop);
+      f32x16 N0, N1;
+      // stage 1
+      softmax(S0, 0, c, mode, nvalid, bias, p0);
+      if (more) N0 = qk(kop, 0);
+      if (c > 0) pv(vop_p, p1, 1);
+      interleave(c > 0 ? 2 * C::KS : C::KS);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage 2
+      bf16x8 vop_n[C::MT][2];
+      if (more) load_vop(vt, c + 1, vop_n);
+      softmax(S1, 1, c, mode, nvalid, bias, p1);
+      if (more) N1 = qk(kop, 1);
+      pv(vop_c, p0, 0);
+      interleave(C::KS + 2 * C::MT);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        vop_p[mt][0] = vop_c[mt][0];
+        vop_p[mt][1] = vop_c[mt][1];
+        if (more) {
+          vop_c[mt][0] = vop_n[mt][0];
+          vop_c[mt][1] = vop_n[mt][1];
+        }
+      }
+      if (more) {
+        S0 = N0;
+        S1 = N1;
+      }
+    }
+    pv(vop_p, p1, 1);
   };
 
   // ---- kept blocks (sparse) or all blocks j <= i (dense)
@@ -313,32 +384,44 @@ void attn_kernel(AttnArgs a) {
       __syncthreads();
       issue_load(j0, 0);
     }
-    for (int n = 0; n < nblk; ++n) {
+    // Blocks 0 .. nblk-2 are strictly below the diagonal (the list is
+    // ascending and ends with block i): one unmasked loop, the diagonal block
+    // peeled after it.  List entries are read two blocks ahead so that the
+    // address of the next K/V prefetch never waits on memory.
+    int jnext = nblk > 1 ? (a.sparse ? list[1] : 1) : 0;
+    for (int n = 0; n + 1 < nblk; ++n) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (n + 1 < nblk) issue_load(a.sparse ? list[n + 1] : n + 1, (n + 1) & 1);
-      const int j = a.sparse ? list[n] : n;
+      const int jafter = n + 2 < nblk ? (a.sparse ? list[n + 2] : n + 2) : 0;
+      issue_load(jnext, (n + 1) & 1);
       const char* kt = lds + (n & 1) * C::TILE;
       const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      if (j == i) {
-#pragma unroll 1
-        for (int kc = 0; kc < C::KC; ++kc) chunk(kt, vt, kc, 1, 0, 0.f);
-      } else {
-#pragma unroll 1
-        for (int kc = 0; kc < C::KC; ++kc) chunk(kt, vt, kc, 0, 0, 0.f);
-      }
+      run_tile(kt, vt, C::KC, 0, 0, 0.f);
+      jnext = jafter;
     }
+    {
+      const int n = nblk - 1;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const char* kt = lds + (n & 1) * C::TILE;
+      const char* vt = lds + (2 + (n & 1)) * C::TILE;
+      run_tile(kt, vt, C::KC, 1, 0, 0.f);
+    }
+
     // ---- mean correction: dropped blocks as pseudo-keys
-    // LDS during this phase: pseudo-K tile (32 rows) | pseudo-V tile (32 rows) |
-    // ndrop | kept-block bitmap | dropped-block list.
+    // LDS during this phase: pseudo-K tile (32 rows, bf16) | pseudo-V tile |
+    // ndrop | kept-block bitmap | dropped-block list | 2 staging buffers of
+    // the fp32 kbar/vbar rows of a 32-pseudo-key chunk (global_load_lds,
+    // one chunk ahead of the compute).
     if (a.sparse && a.mean_correction && i > 0) {
       __syncthreads();
       char* pk_t = lds;
-      char* pv_t = lds + 32 * C::RS;
-      int* ndrop_slot = (int*)(lds + 64 * C::RS);
+      char* pv_t = lds + C::PSB;
+      int* ndrop_slot = (int*)(lds + 2 * C::PSB);
       uint32_t* bm = (uint32_t*)(ndrop_slot + 1);
       const int nwords = (i + 31) >> 5;
       int* drop = (int*)(bm + nwords);
+      char* stage = lds + corr_stage_offset<D, BLK>(a.seq.nkb_stride);
       for (int w = tid; w < nwords; w += nthr) bm[w] = 0u;
       __syncthreads();
       for (int n = tid; n < nblk; n += nthr) {
@@ -372,27 +455,37 @@ void attn_kernel(AttnArgs a) {
       const float* kbr = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
       const float* vbr = a.vbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
       const float bias = log2f((float)BLK);  // ln(n_j) in log2 units; dropped blocks are full
-      constexpr int CH8 = D / 8;             // 8-element pieces per row
-      for (int c0 = 0; c0 < ndrop; c0 += 32) {
+      // stage chunk c (32 rows of kbar then 32 rows of vbar, fp32) into buffer bb
+      auto stage_load = [&](int c0, int bb) __attribute__((always_inline)) {
+        constexpr int LPR = D * 4 / 16;        // lanes per fp32 row
+        constexpr int RPO = 64 / LPR;          // rows per wave op
+        for (int it = wave; it < 64 / RPO; it += nthr >> 6) {
+          const int rr = it * RPO + lane / LPR;   // 0..63: K rows then V rows
+          const int r32 = rr & 31;
+          const int id = c0 + r32 < ndrop ? drop[c0 + r32] : 0;
+          const float* src = (rr < 32 ? kbr : vbr) + (long)id * D + (lane % LPR) * 4;
+          __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + bb * C::STG + it * 1024), 16, 0,
+                                           0);
+        }
+      };
+      constexpr int CH8 = D / 8;  // 8-element pieces per row
+      if (ndrop > 0) stage_load(0, 0);
+      for (int c0 = 0, cc = 0; c0 < ndrop; c0 += 32, ++cc) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (c0 + 32 < ndrop) stage_load(c0 + 32, (cc + 1) & 1);
+        const char* sb = stage + (cc & 1) * C::STG;
         for (int task = tid; task < 2 * 32 * CH8; task += nthr) {
-          const int tensor = task / (32 * CH8);
-          const int rem = task - tensor * 32 * CH8;
-          const int rr = rem / CH8;
-          const int c = rem - rr * CH8;
-          uint4 w = make_uint4(0u, 0u, 0u, 0u);
-          if (c0 + rr < ndrop) {
-            const int id = drop[c0 + rr];
-            const float4* src = (const float4*)((tensor ? vbr : kbr) + (long)id * D + c * 8);
-            const float4 x0 = src[0];
-            const float4 x1 = src[1];
-            w = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                           pack_bf16x2(x1.z, x1.w));
-          }
-          *(uint4*)((tensor ? pv_t : pk_t) + rr * C::RS + c * 16) = w;
+          const int rr = task / CH8;            // 0..63
+          const int c = task - rr * CH8;
+          const float4 x0 = *(const float4*)(sb + rr * D * 4 + c * 32);
+          const float4 x1 = *(const float4*)(sb + rr * D * 4 + c * 32 + 16);
+          const uint4 w = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
+                                     pack_bf16x2(x1.z, x1.w));
+          *(uint4*)((rr < 32 ? pk_t : pv_t) + (rr & 31) * C::RS + c * 16) = w;
         }
         __syncthreads();
-        chunk(pk_t, pv_t, 0, 2, min(32, ndrop - c0), bias);
-        __syncthreads();
+        run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias);
       }
     }
 
@@ -457,7 +550,7 @@ template <int D, int BLK>
 static size_t attn_lds_bytes(int nkb) {
   using C = Cfg<D, BLK>;
   size_t lds = 4 * (size_t)C::TILE;
-  const size_t corr = 64 * (size_t)C::RS + 4 + 4 * (size_t)((nkb + 31) / 32) + 4 * (size_t)nkb;
+  const size_t corr = (size_t)corr_stage_offset<D, BLK>(nkb) + 2 * (size_t)C::STG;
   return corr > lds ? corr : lds;
 }
 
