@@ -51,11 +51,36 @@ def flops(cnt, hq, hkv, d, b, S):
                 executed_attn=executed_attn, executed_corr=executed_corr, dense_eq=dense_eq, dense_exec=dense_exec)
 
 
-def cpu_baseline(prob, hkv, b, tau, n_blocks=3, seed=0):
-    """Time the float64 oracle on a bounded sample of the workload: pooling and
-    selection of one KV group over the whole sequence, attention for a seeded
-    sample of query blocks; extrapolated to one layer (all groups, all query
-    blocks) in ms."""
+def kernel_source_hash():
+    """Hash of the HIP sources; HBM traffic read from profiles/ is reported only
+    if it was measured on the same sources."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_long_scores_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per sparse-attention launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, scaled by the copy-kernel calibration; None
+    when the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "attn_sparse_128k_bf16_traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(prob, hkv, b, tau, n_blocks=256, seed=0):
+    """Time the float64 oracle on a bounded sample of the workload (about 10 s
+    of CPU work): pooling and selection of KV group 0 over the whole sequence,
+    attention of that group for a seeded sample of query blocks; extrapolated
+    to one layer (all groups, all query blocks) in ms."""
     from oracle import attention as A
     try:
         from threadpoolctl import threadpool_info
@@ -99,7 +124,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times), the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        x = torch.ones(1 << 28, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 << 28, "repeats": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (--gpus {args.gpus} requested): the hot path shards by KV head "
               "with no communication, so one GPU's share is what is measured here.", file=sys.stderr)
@@ -211,7 +248,7 @@ def main():
                    "head_dim": d, "block_size": b, "tau": round(tau, 5), "mean_correction": True,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "attn_kernel<128,128> (fp2_sparse_prefill)"},
         "cpu_baseline": cpu,
         "breakdown": {
@@ -226,6 +263,7 @@ def main():
             "eff_tflops_executed_attn": round(achieved, 1),
             "dense": res_dense,
             "speedup_vs_dense": round(res_dense["ms"] / step_ms, 2) if res_dense else None,
+            "kernel_source_hash": kernel_source_hash(),
         },
     }
     print(json.dumps(line), flush=True)
