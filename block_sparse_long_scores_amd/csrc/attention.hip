@@ -294,51 +294,46 @@ void attn_kernel(AttnArgs a) {
   //   stage 1: softmax(S_c, columns 0)  ||  QK(c+1, columns 0), PV(c-1, columns 1)
   //   stage 2: softmax(S_c, columns 1)  ||  QK(c+1, columns 1), PV(c, columns 0)
   // so the exp/sum/convert VALU work of one column set runs under the MFMAs of
-  // the other; PV(last, columns 1) closes the tile.
+  // the other; PV(last, columns 1) closes the tile.  Operand buffers are
+  // indexed by chunk parity (no register copies after unrolling), and the
+  // tile base offsets go through readfirstlane so every LDS operand address
+  // is one base register plus a 16-bit immediate.
   auto run_tile = [&](const char* kt, const char* vt, int nch, int mode, int nvalid, float bias)
       __attribute__((always_inline)) {
+    const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
+    const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
+    const char* kbase = lds + kbo;
+    const char* vbase = lds + vbo;
     bf16x8 kop[C::KS];
-    bf16x8 vop_c[C::MT][2], vop_p[C::MT][2];
-    bf16x8 p0[2], p1[2];
-    load_kop(kt, 0, kop);
-    load_vop(vt, 0, vop_c);
-    f32x16 S0 = qk(kop, 0);
-    f32x16 S1 = qk(kop, 1);
+    bf16x8 vop[2][C::MT][2];
+    bf16x8 p0[2], p1[2][2];
+    f32x16 S[2][2];
+    load_kop(kbase, 0, kop);
+    load_vop(vbase, 0, vop[0]);
+    S[0][0] = qk(kop, 0);
+    S[0][1] = qk(kop, 1);
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
       if (c >= nch) break;
+      const int cp = c & 1, np = cp ^ 1;
       const bool more = c + 1 < nch;
-      if (more) load_kop(kt, c + 1, kop);
-      f32x16 N0, N1;
+      if (more) load_kop(kbase, c + 1, kop);
       // stage 1
-      softmax(S0, 0, c, mode, nvalid, bias, p0);
-      if (more) N0 = qk(kop, 0);
-      if (c > 0) pv(vop_p, p1, 1);
+      softmax(S[cp][0], 0, c, mode, nvalid, bias, p0);
+      if (more) S[np][0] = qk(kop, 0);
+      if (c > 0) pv(vop[np], p1[np], 1);
       interleave(c > 0 ? 2 * C::KS : C::KS);
       __builtin_amdgcn_sched_barrier(0);
       // stage 2
-      bf16x8 vop_n[C::MT][2];
-      if (more) load_vop(vt, c + 1, vop_n);
-      softmax(S1, 1, c, mode, nvalid, bias, p1);
-      if (more) N1 = qk(kop, 1);
-      pv(vop_c, p0, 0);
+      if (more) load_vop(vbase, c + 1, vop[np]);
+      softmax(S[cp][1], 1, c, mode, nvalid, bias, p1[cp]);
+      if (more) S[np][1] = qk(kop, 1);
+      pv(vop[cp], p0, 0);
       interleave(C::KS + 2 * C::MT);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        vop_p[mt][0] = vop_c[mt][0];
-        vop_p[mt][1] = vop_c[mt][1];
-        if (more) {
-          vop_c[mt][0] = vop_n[mt][0];
-          vop_c[mt][1] = vop_n[mt][1];
-        }
-      }
-      if (more) {
-        S0 = N0;
-        S1 = N1;
-      }
     }
-    pv(vop_p, p1, 1);
+    const int lp = (nch - 1) & 1;
+    pv(vop[lp], p1[lp], 1);
   };
 
   // ---- kept blocks (sparse) or all blocks j <= i (dense)
