@@ -172,7 +172,8 @@ def fp2_version():
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"), softmax_scale=0.0,
                 mean_correction=True, fp8=False, out_fp32=False, q_scale=None, k_scale=None, v_scale=None):
-    """Build an ``Fp2Params``; fp8 scales are device fp32 tensors (kept alive by the caller)."""
+    """Build an ``Fp2Params``; fp8 scales are device fp32 tensors.  The params
+    object holds references to them, so they live as long as it does."""
     p = Fp2Params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -186,6 +187,7 @@ def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"
     p.q_scale = q_scale.data_ptr() if q_scale is not None else None
     p.k_scale = k_scale.data_ptr() if k_scale is not None else None
     p.v_scale = v_scale.data_ptr() if v_scale is not None else None
+    p._scale_tensors = (q_scale, k_scale, v_scale)
     return p
 
 

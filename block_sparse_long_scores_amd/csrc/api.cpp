@@ -93,8 +93,8 @@ int select_rows_per_wg(int D, int nkb) {
   return 0;
 }
 
-bool attn_lds_ok(int D, int block, int nkb) {
-  const size_t need = attention_lds_bytes(D, block, nkb);
+bool attn_lds_ok(int D, int block, int nkb, int fp8) {
+  const size_t need = attention_lds_bytes(D, block, nkb, fp8);
   return need > 0 && need <= 160 * 1024;
 }
 
@@ -207,11 +207,10 @@ static fp2_status attention_common(const fp2_params* p, int32_t batch, int32_t s
   if (sparse && (!block_idx || !block_cnt)) return fail(FP2_EINVAL, "block_idx and block_cnt must be non-NULL");
   if (corr && (!pooled_k || !pooled_v))
     return fail(FP2_EINVAL, "mean_correction needs pooled_k and pooled_v");
-  if (p->in_dtype == FP2_FP8_E4M3) return fail(FP2_EUNSUPPORTED, "fp8 attention is not built in this version");
   const int D = p->head_dim, b = p->block_size;
   const int nqb = nq_blocks(seqlen_q, seqlen_k, b);
   const int nkb = nk_blocks(seqlen_k, b);
-  if (!attn_lds_ok(D, b, nkb)) return fail(FP2_EUNSUPPORTED, "seqlen_k=%d too long for the attention kernel", seqlen_k);
+  if (!attn_lds_ok(D, b, nkb, p->in_dtype == FP2_FP8_E4M3)) return fail(FP2_EUNSUPPORTED, "seqlen_k=%d too long for the attention kernel", seqlen_k);
   AttnArgs a{};
   fill_attn_common(a, p);
   a.seq = SeqDesc{batch, seqlen_q, seqlen_k, nullptr, nullptr, nqb, nkb};
@@ -312,11 +311,10 @@ fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const
   if ((long)max_pages_per_seq * page_size < max_seqlen_k)
     return fail(FP2_EINVAL, "max_pages_per_seq=%d * page_size=%d < max_seqlen_k=%d", max_pages_per_seq, page_size,
                 max_seqlen_k);
-  if (p->in_dtype == FP2_FP8_E4M3) return fail(FP2_EUNSUPPORTED, "fp8 attention is not built in this version");
   int max_nqb, max_nkb;
   fp2_paged_mask_dims(p, max_seqlen_q, max_seqlen_k, &max_nqb, &max_nkb);
   const int tq = select_rows_per_wg(D, max_nkb);
-  if (tq == 0 || !attn_lds_ok(D, b, max_nkb))
+  if (tq == 0 || !attn_lds_ok(D, b, max_nkb, p->in_dtype == FP2_FP8_E4M3))
     return fail(FP2_EUNSUPPORTED, "max_seqlen_k=%d too long for this build", max_seqlen_k);
   const PagedLayout L = paged_layout(p, num_seqs, max_nqb, max_nkb);
   if (!workspace || workspace_bytes < L.total)

@@ -44,6 +44,8 @@
 #include "fp2_internal.h"
 #include "geometry.h"
 
+#include <type_traits>
+
 namespace fp2 {
 
 constexpr int kRowsPerWave = 64;
@@ -53,26 +55,31 @@ constexpr float kRefMargin = 16.0f;     // log2 units above the sink-chunk max
 constexpr float kRefOverflow = 100.0f;  // log2 of the normaliser that forces a rerun
 constexpr int kMaxPasses = 4;
 
-template <int D, int BLK>
+template <int D, int BLK, bool F8>
 struct Cfg {
-  static constexpr int KS = D / 16;            // k-steps of the QK MFMA along d
+  static constexpr int ESZ = F8 ? 1 : 2;       // bytes per K/V element
+  static constexpr int KS = D / 16;            // k-steps of a bf16 QK chain (32x32x16)
+  static constexpr int KS8 = D / 64;           // k-steps of an fp8 QK chain (32x32x64)
   static constexpr int MT = D / 32;            // 32-row tiles of O^T along d
   static constexpr int KC = BLK / 32;          // 32-key chunks per block
-  static constexpr int ROWB = D * 2;           // bytes of one bf16 row
-  // LDS row stride: rows are padded so that the 8 rows of a ds_read_b128
-  // phase and the 4 rows of a ds_read_b64_tr_b16 group land on distinct banks.
-  static constexpr int RS = ROWB + (D == 128 ? 32 : 16);
+  static constexpr int NSC = BLK / 64;         // 64-key superchunks per block (fp8 P V)
+  static constexpr int ROWB = D * ESZ;         // bytes of one K/V row of one head
+  // LDS row stride: rows are padded so that the rows read by one LDS read
+  // phase (consecutive rows for the K operand, the 4/8-key groups of the
+  // transpose reads for V) land on distinct banks.
+  static constexpr int RS = F8 ? ROWB + 16 : ROWB + (D == 128 ? 32 : 16);
   static constexpr int TILE = ((BLK * RS + 1023) / 1024) * 1024;  // one K or V tile
   static constexpr int NLD = TILE / 1024;      // global_load_lds wave ops per tile
-  static constexpr int PSB = 32 * RS;          // one 32-row pseudo-key tile (bf16)
+  static constexpr int RS16 = 2 * D + (D == 128 ? 32 : 16);  // bf16 pseudo-key rows
+  static constexpr int PSB = 32 * RS16;        // one 32-row pseudo-key tile (bf16)
   static constexpr int STG = 2 * 32 * D * 4;   // fp32 kbar + vbar rows of one pseudo chunk
 };
 
 // Byte offset of the correction-phase staging buffers (after the pseudo tiles,
 // the count, the bitmap and the dropped list).
-template <int D, int BLK>
+template <int D, int BLK, bool F8>
 __host__ __device__ constexpr int corr_stage_offset(int nkb) {
-  return ((2 * Cfg<D, BLK>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb + 1023) / 1024) * 1024;
+  return ((2 * Cfg<D, BLK, F8>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb + 1023) / 1024) * 1024;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
@@ -125,13 +132,14 @@ __device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[4], const bf16x8 (&
   return S;
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnArgs a) {
-  using C = Cfg<D, BLK>;
+  using C = Cfg<D, BLK, F8>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
+  const int nwaves = nthr >> 6;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
@@ -167,40 +175,69 @@ void attn_kernel(AttnArgs a) {
     off = ((long)(g.qrow0 + r) * a.Hq + (h * G + gq)) * D;
     return (pr < G * BLK) && r >= 0 && r < g.Sq;
   };
+
+  // Q operands (B side of S^T) and the log2-domain scale of a raw score.
+  //  bf16: k-step ks of lane (n, hh) holds d in [16ks + 8hh, +8).
+  //  fp8:  k-step ks of lane (n, hh) holds d in [64ks + 32hh, +32) (the
+  //        32x32x64 MFMA pairs byte e of A lane (x, hh) with byte e of B
+  //        lane (n, hh)); a raw score is in code units and takes the
+  //        per-head dequantization scales q_s * k_s.
+  using QT = typename std::conditional<F8, i32x8, bf16x8>::type;
+  constexpr int QKS = F8 ? C::KS8 : C::KS;
   int rib[NT];
-  bf16x8 qop[NT][C::KS];
+  float cs[NT];
+  QT qop[NT][QKS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     long off;
     const bool ok = qinfo(nt, rib[nt], off);
+    if constexpr (F8) {
+      const unsigned char* qp = (const unsigned char*)a.q + off + 32 * hh;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      if (ok) {
-        qop[nt][ks] = *(const bf16x8*)((const __bf16*)a.q + off + 16 * ks + 8 * hh);
-      } else {
-        qop[nt][ks] = bf16x8{};
+      for (int ks = 0; ks < QKS; ++ks) {
+        if (ok) {
+          const i32x4 lo = *(const i32x4*)(qp + 64 * ks);
+          const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 16);
+          qop[nt][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+          qop[nt][ks] = i32x8{};
+        }
       }
+      const int gq = (pr0 + l32 + 32 * nt) / BLK;
+      cs[nt] = ok ? a.scale_log2 * a.q_scale[h * G + gq] * a.k_scale[h] : a.scale_log2;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < QKS; ++ks) {
+        if (ok) {
+          qop[nt][ks] = *(const bf16x8*)((const __bf16*)a.q + off + 16 * ks + 8 * hh);
+        } else {
+          qop[nt][ks] = bf16x8{};
+        }
+      }
+      cs[nt] = a.scale_log2;
     }
   }
 
   f32x16 O[C::MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) O[mt][nt] = f32x16{};
+  f32x16 Lacc[F8 ? NT : 1];  // fp8: row sums of P, accumulated by MFMA
   float mref[NT], lsum[NT];
 
   // LDS: K tiles at [0, 2*TILE), V tiles at [2*TILE, 4*TILE) (double buffer)
   char* const lds = smem;
   const int rowbytes = a.Hkv * C::ROWB;
   const int Skm1 = g.Sk - 1;
+  const int plog = a.kv.page_log2;
+  const int* ptab = a.kv.page_table ? a.kv.page_table + (long)s * a.kv.max_pages : nullptr;
 
   // K and V tile of key block j -> LDS buffer bb (async, global_load_lds).
   // Wave op `it` fills tile bytes [1024*it, 1024*it + 1024); lane bytes that
   // fall into a row pad (or past the last row) reload chunk 0 of a valid row.
+  // Paged caches: the rows of one wave op span at most two pages when a page
+  // holds 16 rows or more; their two page ids are wave-uniform loads, so no
+  // per-lane load has to complete before the copies are issued.
   auto issue_load = [&](int j, int bb) __attribute__((always_inline)) {
     const int kb0 = j * BLK;
-    for (int it = wave; it < C::NLD; it += nthr >> 6) {
+    for (int it = wave; it < C::NLD; it += nwaves) {
       const int o = it * 1024 + lane * 16;
       int row = o / C::RS;
       const int w = o - row * C::RS;
@@ -210,60 +247,80 @@ void attn_kernel(AttnArgs a) {
         c = 0;
       }
       const int key = min(kb0 + row, Skm1);
-      const char* ks_ = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, key, rowbytes) + h * C::ROWB + c * 16;
-      const char* vs_ = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, key, rowbytes) + h * C::ROWB + c * 16;
-      __builtin_amdgcn_global_load_lds((const void*)ks_, (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vs_, (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024), 16, 0,
-                                       0);
+      long rix;
+      if (ptab) {
+        int pg;
+        if (plog >= 4) {
+          const int klo = min(kb0 + (it * 1024) / C::RS, Skm1);
+          const int khi = min(kb0 + min((it * 1024 + 1023) / C::RS, BLK - 1), Skm1);
+          const int plo = ptab[klo >> plog];
+          const int phi = ptab[khi >> plog];
+          pg = (key >> plog) == (klo >> plog) ? plo : phi;
+        } else {
+          pg = ptab[key >> plog];
+        }
+        rix = ((long)pg << plog) + (key & ((1 << plog) - 1));
+      } else {
+        rix = (long)s * a.seq.seqlen_k + key;
+      }
+      const long boff = rix * rowbytes + h * C::ROWB + c * 16;
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)a.kv.k + boff),
+                                       (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)a.kv.v + boff),
+                                       (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024), 16, 0, 0);
     }
   };
 
-  // Per-lane operand base offsets (bytes, within a tile).
-  //  K (A side of S^T): row l32 of the chunk, 16-byte piece 2*ks + hh.
+  // ===================== bf16 operand path (32x32x16 MFMA) =================
+  // Used for the bf16 K/V tiles and, in both precisions, for the bf16
+  // pseudo-key tiles of the mean correction (row stride RS16).
+  //  K (A side of S^T): row l32 of the chunk; the d-range of k-step ks
+  //  matches the Q operand: bf16 Q [16ks + 8hh, +8); fp8 Q converted to bf16
+  //  [64(ks/4) + 32hh + 8(ks%4), +8).
   //  V (A side of O^T, transpose read): group g = lane/16 reads rows
   //  K0 + (lane%16)/4 at d = 32*mt + 16*(g%2) + 4*(lane%4), K0 = 16*ks2 +
   //  8*sec + 4*hh within the chunk.
-  const int koff = l32 * C::RS + hh * 16;
-  const int voff = (4 * hh + ((lane & 15) >> 2)) * C::RS + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  const int koff16 = l32 * C::RS16 + (F8 ? 64 : 16) * hh;
+  const int voff16 = (4 * hh + ((lane & 15) >> 2)) * C::RS16 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  auto kofs16 = [](int ks) constexpr -> int { return F8 ? 128 * (ks >> 2) + 16 * (ks & 3) : 32 * ks; };
 
-  // K operands of a 32-key chunk (A side of S^T), one 16-byte read per k-step.
   auto load_kop = [&](const char* kt, int kc, bf16x8 (&kop)[C::KS]) __attribute__((always_inline)) {
-    const char* kb = kt + kc * 32 * C::RS + koff;
+    const char* kb = kt + kc * 32 * C::RS16 + koff16;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kop[ks] = *(const bf16x8*)(kb + 32 * ks);
+    for (int ks = 0; ks < C::KS; ++ks) kop[ks] = *(const bf16x8*)(kb + kofs16(ks));
   };
-  // V^T operands of a 32-key chunk (A side of O^T), two transpose reads each.
   auto load_vop = [&](const char* vt, int kc, bf16x8 (&vop)[C::MT][2]) __attribute__((always_inline)) {
-    const char* vb = vt + kc * 32 * C::RS + voff;
+    const char* vb = vt + kc * 32 * C::RS16 + voff16;
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + 16 * ks2 * C::RS));
+            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + 16 * ks2 * C::RS16));
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + (16 * ks2 + 8) * C::RS));
+            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + (16 * ks2 + 8) * C::RS16));
         vop[mt][ks2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
-  auto qk = [&](const bf16x8 (&kop)[C::KS], int nt) __attribute__((always_inline)) -> f32x16 {
+  auto qk = [&](const bf16x8 (&kop)[C::KS], const bf16x8 (&qq)[C::KS]) __attribute__((always_inline)) -> f32x16 {
     f32x16 S = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[nt][ks], S, 0, 0, 0);
+    for (int ks = 0; ks < C::KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qq[ks], S, 0, 0, 0);
     return S;
   };
-  // P = exp2(S*scale - m + bias) as bf16 B-operands, row sums into lsum.
+  // P = exp2(S*cs - m + bias) as bf16 B-operands, row sums into lsum.
   // mode 0: plain; 1: diagonal block (causal mask); 2: pseudo-keys (slots >=
   // nvalid masked).  Key-in-chunk of accumulator register r: 8*(r/4) + 4*hh + r%4.
   auto softmax = [&](const f32x16& S, int nt, int kc, int mode, int nvalid, float bias, bf16x8 (&pk)[2])
       __attribute__((always_inline)) {
     const float mb = mref[nt] - bias;
+    const float sc = F8 ? cs[nt] : a.scale_log2;
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-      float x = __builtin_fmaf(S[r], a.scale_log2, -mb);
+      float x = __builtin_fmaf(S[r], sc, -mb);
       if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
       if (mode == 2 && kic >= nvalid) x = -INFINITY;
       const float p = __builtin_amdgcn_exp2f(x);
@@ -282,14 +339,16 @@ void attn_kernel(AttnArgs a) {
 
   // Interleave hint for one pipeline stage: nmfma MFMAs, each followed by a
   // slice of the stage's VALU work (the softmax of the other column set).
-  auto interleave = [&](int nmfma) __attribute__((always_inline)) {
+  auto interleave = [&](int nmfma, auto nvalu) __attribute__((always_inline)) {
     for (int k = 0; k < nmfma; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);  // VALU
     }
   };
+  using V5 = std::integral_constant<int, 5>;
+  using V16 = std::integral_constant<int, 16>;
 
-  // The NCH 32-key chunks of one K/V tile (or of one pseudo-key tile),
+  // The NCH 32-key chunks of one bf16 K/V tile (or of one pseudo-key tile),
   // software-pipelined in two stages per chunk c:
   //   stage 1: softmax(S_c, columns 0)  ||  QK(c+1, columns 0), PV(c-1, columns 1)
   //   stage 2: softmax(S_c, columns 1)  ||  QK(c+1, columns 1), PV(c, columns 0)
@@ -298,8 +357,8 @@ void attn_kernel(AttnArgs a) {
   // indexed by chunk parity (no register copies after unrolling), and the
   // tile base offsets go through readfirstlane so every LDS operand address
   // is one base register plus a 16-bit immediate.
-  auto run_tile = [&](const char* kt, const char* vt, int nch, int mode, int nvalid, float bias)
-      __attribute__((always_inline)) {
+  auto run_tile = [&](const char* kt, const char* vt, int nch, int mode, int nvalid, float bias,
+                      const bf16x8 (&qq)[NT][C::KS]) __attribute__((always_inline)) {
     const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
     const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
     const char* kbase = lds + kbo;
@@ -310,8 +369,8 @@ void attn_kernel(AttnArgs a) {
     f32x16 S[2][2];
     load_kop(kbase, 0, kop);
     load_vop(vbase, 0, vop[0]);
-    S[0][0] = qk(kop, 0);
-    S[0][1] = qk(kop, 1);
+    S[0][0] = qk(kop, qq[0]);
+    S[0][1] = qk(kop, qq[1]);
 #pragma unroll
     for (int c = 0; c < C::KC; ++c) {
       if (c >= nch) break;
@@ -320,20 +379,180 @@ void attn_kernel(AttnArgs a) {
       if (more) load_kop(kbase, c + 1, kop);
       // stage 1
       softmax(S[cp][0], 0, c, mode, nvalid, bias, p0);
-      if (more) S[np][0] = qk(kop, 0);
+      if (more) S[np][0] = qk(kop, qq[0]);
       if (c > 0) pv(vop[np], p1[np], 1);
-      interleave(c > 0 ? 2 * C::KS : C::KS);
+      interleave(c > 0 ? 2 * C::KS : C::KS, V5{});
       __builtin_amdgcn_sched_barrier(0);
       // stage 2
       if (more) load_vop(vbase, c + 1, vop[np]);
       softmax(S[cp][1], 1, c, mode, nvalid, bias, p1[cp]);
-      if (more) S[np][1] = qk(kop, 1);
+      if (more) S[np][1] = qk(kop, qq[1]);
       pv(vop[cp], p0, 0);
-      interleave(C::KS + 2 * C::MT);
+      interleave(C::KS + 2 * C::MT, V5{});
       __builtin_amdgcn_sched_barrier(0);
     }
     const int lp = (nch - 1) & 1;
     pv(vop[lp], p1[lp], 1);
+  };
+
+  // ===================== fp8 operand path (32x32x64 MFMA) ==================
+  //  K (A side of S^T): lane (x, hh) reads 32 bytes of key row x at d =
+  //  64ks + 32hh, matching the Q operand.
+  //  P^T (B side of O^T): for a 64-key superchunk, bytes 0..15 of lane (n,
+  //  hh) are the accumulator registers of its first 32-key chunk, bytes
+  //  16..31 those of the second, i.e. byte e is key 32(e/16) + 8((e%16)/4) +
+  //  4hh + e%4.  The MFMA's k-block 0 (bytes 0..15 of both lane halves) is
+  //  thus exactly the first chunk and k-block 1 the second, and the E8M0
+  //  scale of k-block kb of column n is read from lane n + 32kb: P is stored
+  //  per (query, chunk) as P' = P * 2^-b with b chosen from the chunk's max,
+  //  so that P' lies in [128, 256) at the max, and 2^b is applied inside the
+  //  MFMA (no fp8 overflow, full e4m3 precision for the largest terms).
+  //  V^T (A side of O^T): ds_read_b64_tr_b8 returns to lane i of a 16-lane
+  //  group byte e = byte i%8 of the row addressed by source lane 2e + i/8, so
+  //  source lanes 2e, 2e+1 address the same key (the P byte order above) at d
+  //  and d + 8; four reads (+16 keys each) fill the 32 bytes.
+  const int koff8 = l32 * C::RS + 32 * hh;
+  const int L16 = lane & 15;
+  const int voff8 = (8 * (L16 >> 3) + 4 * hh + ((L16 >> 1) & 3)) * C::RS + 16 * ((lane >> 4) & 1) + 8 * (L16 & 1);
+  auto load_kop8 = [&](const char* kt, int kc, i32x8 (&kop)[C::KS8]) __attribute__((always_inline)) {
+    const char* kb = kt + kc * 32 * C::RS + koff8;
+#pragma unroll
+    for (int ks = 0; ks < C::KS8; ++ks) {
+      const i32x4 lo = *(const i32x4*)(kb + 64 * ks);
+      const i32x4 hi = *(const i32x4*)(kb + 64 * ks + 16);
+      kop[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto load_vop8 = [&](const char* vt, int sc, i32x8 (&vop)[C::MT]) __attribute__((always_inline)) {
+    const char* vb = vt + sc * 64 * C::RS + voff8;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      i32x2 r[4];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+        r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(vb + 32 * mt + 16 * t4 * C::RS));
+      vop[mt] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    }
+  };
+  auto qk8 = [&](const i32x8 (&kop)[C::KS8], int nt) __attribute__((always_inline)) -> f32x16 {
+    f32x16 S = f32x16{};
+    if constexpr (F8) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS8; ++ks)
+        S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[ks], qop[nt][ks], S, 0, 0, 0, 0, 0, 0);
+    }
+    return S;
+  };
+  // Superchunk softmax of column set nt: Sn[q] is the S^T chunk 2sc + q.
+  // mode 1 applies the causal mask (diagonal block).
+  auto softmax8 = [&](f32x16 (&Sn)[2], int nt, int sc, int mode, i32x8& pk, int& sbyte)
+      __attribute__((always_inline)) {
+    float bias[2];
+    int bq[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (mode == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+          if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
+        }
+      }
+      float m = fmaxf(Sn[q][0], Sn[q][1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(Sn[q][r], Sn[q][r + 1]));
+      m = fmaxf(m, partner32(m));
+      float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
+      fx = fminf(fmaxf(fx, -110.f), 120.f);
+      bq[q] = (int)fx - 7;
+      bias[q] = mref[nt] + (float)bq[q];
+    }
+    sbyte = 127 + (hh ? bq[1] : bq[0]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias[q]));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias[q]));
+        const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias[q]));
+        const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias[q]));
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+        pk[4 * q + j] = w;
+      }
+    }
+  };
+  const i32x8 ones8 = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  auto pv8 = [&](const i32x8 (&vop)[C::MT], const i32x8& pk, int sbyte, int nt) __attribute__((always_inline)) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+        O[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], pk, O[mt][nt], 0, 0, 0, 127, 0, sbyte);
+      Lacc[nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pk, Lacc[nt], 0, 0, 0, 127, 0, sbyte);
+    }
+  };
+  // The NSC superchunks of one fp8 K/V tile, pipelined like run_tile with
+  // 64-key steps:
+  //   stage A: softmax(S_sc, columns 0) || QK(sc+1, columns 0), PV(sc-1, columns 1)
+  //   stage B: softmax(S_sc, columns 1) || QK(sc+1, columns 1), PV(sc, columns 0)
+  auto run_tile8 = [&](const char* kt, const char* vt, int mode) __attribute__((always_inline)) {
+    const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
+    const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
+    const char* kbase = lds + kbo;
+    const char* vbase = lds + vbo;
+    i32x8 kop[2][C::KS8];
+    i32x8 vop[2][C::MT];
+    i32x8 pp0, pp1[2];
+    int sb0, sb1[2];
+    f32x16 S[2][NT][2];
+    load_kop8(kbase, 0, kop[0]);
+    load_kop8(kbase, 1, kop[1]);
+    load_vop8(vbase, 0, vop[0]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      S[0][nt][0] = qk8(kop[0], nt);
+      S[0][nt][1] = qk8(kop[1], nt);
+    }
+#pragma unroll
+    for (int sc = 0; sc < C::NSC; ++sc) {
+      const int cp = sc & 1, np = cp ^ 1;
+      const bool more = sc + 1 < C::NSC;
+      if (more) {
+        load_kop8(kbase, 2 * sc + 2, kop[0]);
+        load_kop8(kbase, 2 * sc + 3, kop[1]);
+      }
+      // stage A
+      softmax8(S[cp][0], 0, sc, mode, pp0, sb0);
+      if (more) {
+        S[np][0][0] = qk8(kop[0], 0);
+        S[np][0][1] = qk8(kop[1], 0);
+      }
+      if (sc > 0) pv8(vop[np], pp1[np], sb1[np], 1);
+      interleave((more ? 2 * C::KS8 : 0) + (sc > 0 ? C::MT + 1 : 0), V16{});
+      __builtin_amdgcn_sched_barrier(0);
+      // stage B
+      if (more) load_vop8(vbase, sc + 1, vop[np]);
+      softmax8(S[cp][1], 1, sc, mode, pp1[cp], sb1[cp]);
+      if (more) {
+        S[np][1][0] = qk8(kop[0], 1);
+        S[np][1][1] = qk8(kop[1], 1);
+      }
+      pv8(vop[cp], pp0, sb0, 0);
+      interleave((more ? 2 * C::KS8 : 0) + C::MT + 1, V16{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int lp = (C::NSC - 1) & 1;
+    pv8(vop[lp], pp1[lp], sb1[lp], 1);
+  };
+
+  auto run_main = [&](const char* kt, const char* vt, int mode) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      run_tile8(kt, vt, mode);
+    } else {
+      run_tile(kt, vt, C::KC, mode, 0, 0.f, qop);
+    }
   };
 
   // ---- kept blocks (sparse) or all blocks j <= i (dense)
@@ -348,16 +567,25 @@ void attn_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   {
-    bf16x8 kop[C::KS];
-    load_kop(lds, 0, kop);
+    f32x16 S0[NT];
+    if constexpr (F8) {
+      i32x8 kop[C::KS8];
+      load_kop8(lds, 0, kop);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) S0[nt] = qk8(kop, nt);
+    } else {
+      bf16x8 kop[C::KS];
+      load_kop(lds, 0, kop);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) S0[nt] = qk_chain(kop, qop[nt]);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const f32x16 S = qk_chain(kop, qop[nt]);
       float m = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-        float x = S[r] * a.scale_log2;
+        float x = S0[nt][r] * cs[nt];
         if (j0 == i && kic > rib[nt]) x = -INFINITY;
         m = fmaxf(m, x);
       }
@@ -370,11 +598,12 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll 1
   for (int pass = 0; pass < kMaxPasses; ++pass) {
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) O[mt][nt] = f32x16{};
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lsum[nt] = 0.f;
+      for (int mt = 0; mt < C::MT; ++mt) O[mt][nt] = f32x16{};
+      lsum[nt] = 0.f;
+      if constexpr (F8) Lacc[nt] = f32x16{};
+    }
     if (pass > 0) {
       __syncthreads();
       issue_load(j0, 0);
@@ -391,7 +620,7 @@ void attn_kernel(AttnArgs a) {
       issue_load(jnext, (n + 1) & 1);
       const char* kt = lds + (n & 1) * C::TILE;
       const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      run_tile(kt, vt, C::KC, 0, 0, 0.f);
+      run_main(kt, vt, 0);
       jnext = jafter;
     }
     {
@@ -400,14 +629,17 @@ void attn_kernel(AttnArgs a) {
       __syncthreads();
       const char* kt = lds + (n & 1) * C::TILE;
       const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      run_tile(kt, vt, C::KC, 1, 0, 0.f);
+      run_main(kt, vt, 1);
     }
 
     // ---- mean correction: dropped blocks as pseudo-keys
     // LDS during this phase: pseudo-K tile (32 rows, bf16) | pseudo-V tile |
     // ndrop | kept-block bitmap | dropped-block list | 2 staging buffers of
     // the fp32 kbar/vbar rows of a 32-pseudo-key chunk (global_load_lds,
-    // one chunk ahead of the compute).
+    // one chunk ahead of the compute).  In fp8 the pseudo rows are divided
+    // by the head's k / v scale so that they share the code units of the
+    // fp8 K and V (the logit scale cs and the output scale v_s then apply
+    // to both), and Q is widened to bf16 (exact for e4m3 values).
     if (a.sparse && a.mean_correction && i > 0) {
       __syncthreads();
       char* pk_t = lds;
@@ -416,7 +648,7 @@ void attn_kernel(AttnArgs a) {
       uint32_t* bm = (uint32_t*)(ndrop_slot + 1);
       const int nwords = (i + 31) >> 5;
       int* drop = (int*)(bm + nwords);
-      char* stage = lds + corr_stage_offset<D, BLK>(a.seq.nkb_stride);
+      char* stage = lds + corr_stage_offset<D, BLK, F8>(a.seq.nkb_stride);
       for (int w = tid; w < nwords; w += nthr) bm[w] = 0u;
       __syncthreads();
       for (int n = tid; n < nblk; n += nthr) {
@@ -450,11 +682,28 @@ void attn_kernel(AttnArgs a) {
       const float* kbr = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
       const float* vbr = a.vbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
       const float bias = log2f((float)BLK);  // ln(n_j) in log2 units; dropped blocks are full
+      const float kmul = F8 ? 1.f / a.k_scale[h] : 1.f;
+      const float vmul = F8 ? 1.f / a.v_scale[h] : 1.f;
+      bf16x8 q16[NT][C::KS];
+      if constexpr (F8) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const i32x8 w = qop[nt][ks >> 2];
+            const uint32_t w0 = (uint32_t)w[2 * (ks & 3)], w1 = (uint32_t)w[2 * (ks & 3) + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              q16[nt][ks][e] = (__bf16)fp8_byte_to_f32(w0, e);
+              q16[nt][ks][4 + e] = (__bf16)fp8_byte_to_f32(w1, e);
+            }
+          }
+      }
       // stage chunk c (32 rows of kbar then 32 rows of vbar, fp32) into buffer bb
       auto stage_load = [&](int c0, int bb) __attribute__((always_inline)) {
         constexpr int LPR = D * 4 / 16;        // lanes per fp32 row
         constexpr int RPO = 64 / LPR;          // rows per wave op
-        for (int it = wave; it < 64 / RPO; it += nthr >> 6) {
+        for (int it = wave; it < 64 / RPO; it += nwaves) {
           const int rr = it * RPO + lane / LPR;   // 0..63: K rows then V rows
           const int r32 = rr & 31;
           const int id = c0 + r32 < ndrop ? drop[c0 + r32] : 0;
@@ -473,14 +722,19 @@ void attn_kernel(AttnArgs a) {
         for (int task = tid; task < 2 * 32 * CH8; task += nthr) {
           const int rr = task / CH8;            // 0..63
           const int c = task - rr * CH8;
+          const float f = rr < 32 ? kmul : vmul;
           const float4 x0 = *(const float4*)(sb + rr * D * 4 + c * 32);
           const float4 x1 = *(const float4*)(sb + rr * D * 4 + c * 32 + 16);
-          const uint4 w = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                                     pack_bf16x2(x1.z, x1.w));
-          *(uint4*)((rr < 32 ? pk_t : pv_t) + (rr & 31) * C::RS + c * 16) = w;
+          const uint4 w = make_uint4(pack_bf16x2(x0.x * f, x0.y * f), pack_bf16x2(x0.z * f, x0.w * f),
+                                     pack_bf16x2(x1.x * f, x1.y * f), pack_bf16x2(x1.z * f, x1.w * f));
+          *(uint4*)((rr < 32 ? pk_t : pv_t) + (rr & 31) * C::RS16 + c * 16) = w;
         }
         __syncthreads();
-        run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias);
+        if constexpr (F8) {
+          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, q16);
+        } else {
+          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, qop);
+        }
       }
     }
 
@@ -490,7 +744,7 @@ void attn_kernel(AttnArgs a) {
     bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float lt = lsum[nt] + partner32(lsum[nt]);
+      const float lt = (F8 ? Lacc[nt][0] : 0.f) + lsum[nt] + partner32(lsum[nt]);
       if (!(lt < __builtin_exp2f(kRefOverflow))) {
         bad = true;
         mref[nt] += (lt < INFINITY) ? log2f(lt) : kRefOverflow;
@@ -499,15 +753,16 @@ void attn_kernel(AttnArgs a) {
     if (!__syncthreads_or(bad)) break;
   }
 
-  // ---- epilogue: O = O^T / l, LSE
+  // ---- epilogue: O = O^T / l (fp8: times the head's v scale), LSE
   const bool out32 = a.out_fp32;
+  const float oscale = F8 ? a.v_scale[h] : 1.f;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     int rb;
     long off;
     const bool ok = qinfo(nt, rb, off);
-    const float lt = lsum[nt] + partner32(lsum[nt]);
-    const float inv = 1.f / lt;
+    const float lt = (F8 ? Lacc[nt][0] : 0.f) + lsum[nt] + partner32(lsum[nt]);
+    const float inv = oscale / lt;
     if (ok) {
       if (a.lse && hh == 0) {
         const int gq = (pr0 + l32 + 32 * nt) / BLK;
@@ -541,41 +796,54 @@ void attn_kernel(AttnArgs a) {
 }
 
 // LDS bytes the attention kernel needs for a given key-block count.
-template <int D, int BLK>
+template <int D, int BLK, bool F8>
 static size_t attn_lds_bytes(int nkb) {
-  using C = Cfg<D, BLK>;
+  using C = Cfg<D, BLK, F8>;
   size_t lds = 4 * (size_t)C::TILE;
-  const size_t corr = (size_t)corr_stage_offset<D, BLK>(nkb) + 2 * (size_t)C::STG;
+  const size_t corr = (size_t)corr_stage_offset<D, BLK, F8>(nkb) + 2 * (size_t)C::STG;
   return corr > lds ? corr : lds;
 }
 
-template <int D, int BLK>
+template <int D, int BLK, bool F8>
 static hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const long nwg = (long)a.Hkv * a.seq.batch * a.parts * a.nqb_grid;
-  const size_t lds = attn_lds_bytes<D, BLK>(a.seq.nkb_stride);
+  const size_t lds = attn_lds_bytes<D, BLK, F8>(a.seq.nkb_stride);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, BLK>), dim3((unsigned)nwg), dim3(64 * a.waves), lds, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, BLK, F8>), dim3((unsigned)nwg), dim3(64 * a.waves), lds, st, a);
   return hipGetLastError();
 }
 
-size_t attention_lds_bytes(int D, int block, int nkb) {
-  if (D == 128 && block == 128) return attn_lds_bytes<128, 128>(nkb);
-  if (D == 128 && block == 64) return attn_lds_bytes<128, 64>(nkb);
-  if (D == 64 && block == 128) return attn_lds_bytes<64, 128>(nkb);
-  if (D == 64 && block == 64) return attn_lds_bytes<64, 64>(nkb);
+size_t attention_lds_bytes(int D, int block, int nkb, int fp8) {
+  if (fp8) {
+    if (D == 128 && block == 128) return attn_lds_bytes<128, 128, true>(nkb);
+    if (D == 128 && block == 64) return attn_lds_bytes<128, 64, true>(nkb);
+    if (D == 64 && block == 128) return attn_lds_bytes<64, 128, true>(nkb);
+    if (D == 64 && block == 64) return attn_lds_bytes<64, 64, true>(nkb);
+    return 0;
+  }
+  if (D == 128 && block == 128) return attn_lds_bytes<128, 128, false>(nkb);
+  if (D == 128 && block == 64) return attn_lds_bytes<128, 64, false>(nkb);
+  if (D == 64 && block == 128) return attn_lds_bytes<64, 128, false>(nkb);
+  if (D == 64 && block == 64) return attn_lds_bytes<64, 64, false>(nkb);
   return 0;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t st) {
-  if (fp8) return hipErrorNotSupported;
-  if (D == 128 && block == 128) return launch_t<128, 128>(a, st);
-  if (D == 128 && block == 64) return launch_t<128, 64>(a, st);
-  if (D == 64 && block == 128) return launch_t<64, 128>(a, st);
-  if (D == 64 && block == 64) return launch_t<64, 64>(a, st);
+  if (fp8) {
+    if (D == 128 && block == 128) return launch_t<128, 128, true>(a, st);
+    if (D == 128 && block == 64) return launch_t<128, 64, true>(a, st);
+    if (D == 64 && block == 128) return launch_t<64, 128, true>(a, st);
+    if (D == 64 && block == 64) return launch_t<64, 64, true>(a, st);
+    return hipErrorNotSupported;
+  }
+  if (D == 128 && block == 128) return launch_t<128, 128, false>(a, st);
+  if (D == 128 && block == 64) return launch_t<128, 64, false>(a, st);
+  if (D == 64 && block == 128) return launch_t<64, 128, false>(a, st);
+  if (D == 64 && block == 64) return launch_t<64, 64, false>(a, st);
   return hipErrorNotSupported;
 }
 

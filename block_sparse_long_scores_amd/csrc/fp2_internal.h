@@ -82,6 +82,6 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t s);
 // Dynamic LDS bytes of the attention kernel (0 for an unsupported shape).
-size_t attention_lds_bytes(int D, int block, int nkb);
+size_t attention_lds_bytes(int D, int block, int nkb, int fp8);
 
 }  // namespace fp2

@@ -146,14 +146,21 @@ def make_problem(kind, seed, seqlen_k, hq, hkv, d, block, seqlen_q=None,
 E4M3_MAX = 448.0
 
 
-def quantize_e4m3(x, head_axis):
-    """Per-head amax calibration: scale_h = amax_h / 448 (1 if amax_h = 0);
-    code = RNE(x / scale_h) saturated to +-448.  Returns (uint8 codes tensor,
-    float32 scales tensor).  The cast is torch's float8_e4m3fn conversion."""
+def e4m3_scales(x, head_axis):
+    """Per-head amax calibration: scale_h = amax_h / 448 (1 if amax_h = 0)."""
     xf = x.float()
     dims = [a for a in range(xf.dim()) if a != head_axis]
     amax = xf.abs().amax(dim=dims)
-    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    return torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).float()
+
+
+def quantize_e4m3(x, head_axis, scale=None):
+    """code = RNE(x / scale_h) saturated to +-448, with per-head scales from
+    e4m3_scales unless given.  Returns (uint8 codes tensor, float32 scales
+    tensor).  The cast is torch's float8_e4m3fn conversion."""
+    xf = x.float()
+    if scale is None:
+        scale = e4m3_scales(xf, head_axis)
     shape = [1] * xf.dim()
     shape[head_axis] = -1
     y = (xf / scale.reshape(shape)).clamp(-E4M3_MAX, E4M3_MAX)
@@ -182,15 +189,20 @@ class PagedBatch:
     block: int
     seqs: list                 # per sequence: dict(q, k, v) logical bf16 tensors
     canary_pages: np.ndarray
+    q_scale: torch.Tensor = None  # fp8 batches: per-head scales [Hq], [Hkv], [Hkv]
+    k_scale: torch.Tensor = None
+    v_scale: torch.Tensor = None
 
 
 def make_paged(seed, kv_lens, q_lens, hq, hkv, d, block, page_size=64,
-               kind="planted", n_canary=64):
+               kind="planted", n_canary=64, fp8=False):
     """Continuous batch: sequence s has kv_lens[s] tokens in the cache, the
     last q_lens[s] of them new (query rows).  Sequence s is generated at its
     full length from stream s+1.  Physical pages are a seeded permutation of
     num_pages + n_canary pages; the canary pages hold NaN and are never
-    referenced; unused page-table entries point at a canary page."""
+    referenced; unused page-table entries point at a canary page.
+    fp8: q and the caches become e4m3 codes with per-head scales calibrated
+    over the whole batch; each seqs entry also gets its codes (qc, kc, vc)."""
     n = len(kv_lens)
     pages_per = [-(-L // page_size) for L in kv_lens]
     num_pages = sum(pages_per)
@@ -220,9 +232,23 @@ def make_paged(seed, kv_lens, q_lens, hq, hkv, d, block, page_size=64,
             v_cache[phys, :b - a] = pr.v[a:b]
     cu = np.zeros(n + 1, dtype=np.int32)
     cu[1:] = np.cumsum(q_lens)
-    return PagedBatch(torch.cat(qs, 0), torch.from_numpy(cu),
+    q = torch.cat(qs, 0)
+    scales = (None, None, None)
+    if fp8:
+        qsc = e4m3_scales(q, 1)
+        ksc = e4m3_scales(torch.cat([x["k"] for x in seqs], 0), 1)
+        vsc = e4m3_scales(torch.cat([x["v"] for x in seqs], 0), 1)
+        q = quantize_e4m3(q, 1, qsc)[0]
+        k_cache = quantize_e4m3(k_cache, 2, ksc)[0]   # NaN canaries stay NaN codes
+        v_cache = quantize_e4m3(v_cache, 2, vsc)[0]
+        for x in seqs:
+            x["qc"] = quantize_e4m3(x["q"], 1, qsc)[0]
+            x["kc"] = quantize_e4m3(x["k"], 1, ksc)[0]
+            x["vc"] = quantize_e4m3(x["v"], 1, vsc)[0]
+        scales = (qsc, ksc, vsc)
+    return PagedBatch(q, torch.from_numpy(cu),
                       torch.tensor(kv_lens, dtype=torch.int32), k_cache, v_cache,
-                      torch.from_numpy(table), page_size, block, seqs, canary)
+                      torch.from_numpy(table), page_size, block, seqs, canary, *scales)
 
 
 # ---------------------------------------------------------------- workloads
