@@ -5,9 +5,13 @@ workload (batch 1, 32 query / 8 KV heads, head_dim 128, block 128, planted
 retrieval structure + RoPE, tau for ~80% block sparsity): fp2_select_blocks
 (pool + score + select) followed by fp2_sparse_prefill (attention with mean
 correction).  The in-house dense causal kernel runs on the same inputs for the
-speedup.  Prints ONE JSON line.
+speedup.  The same run also times, as breakdown entries, the FP8 variant of the
+128K layer (e4m3 inputs with per-head scales) at ~80/85/90% sparsity against
+the FP8 dense kernel, and the paged-KV continuous batch of six sequences
+(4K..128K, two chunked prefills over cached prefixes).  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-dense]
+                    [--no-fp8] [--no-paged]
 """
 
 import argparse
@@ -76,11 +80,12 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(prob, hkv, b, tau, n_blocks=256, seed=0):
-    """Time the float64 oracle on a bounded sample of the workload (about 10 s
-    of CPU work): pooling and selection of KV group 0 over the whole sequence,
-    attention of that group for a seeded sample of query blocks; extrapolated
-    to one layer (all groups, all query blocks) in ms."""
+def cpu_baseline(prob, hkv, b, tau, budget_s=12.0, seed=0):
+    """Time the float64 oracle on a bounded sample of the workload (about
+    10-30 s of CPU work): pooling and selection of KV group 0 over the whole
+    sequence, then attention of that group for seeded random query blocks, 8 at
+    a time, until the time budget is spent; extrapolated to one layer (all KV
+    groups, all query blocks, by kept-block count) in ms."""
     from oracle import attention as A
     try:
         from threadpoolctl import threadpool_info
@@ -89,7 +94,6 @@ def cpu_baseline(prob, hkv, b, tau, n_blocks=256, seed=0):
         threads = os.cpu_count()
     S = prob.q.shape[0]
     G = prob.q.shape[1] // hkv
-    t0 = time.perf_counter()
     q = prob.q[:, :G].float().numpy()
     k = prob.k[:, :1].float().numpy()
     v = prob.v[:, :1].float().numpy()
@@ -99,20 +103,176 @@ def cpu_baseline(prob, hkv, b, tau, n_blocks=256, seed=0):
     Sc = A.block_scores(qbar, kbar, geo.q_block_ids())
     kept, _ = A.select(Sc, geo.q_block_ids(), tau)
     t2 = time.perf_counter()
-    rng = np.random.default_rng(seed)
-    blocks = sorted(rng.choice(geo.nqb, size=n_blocks, replace=False).tolist())
-    A.attend(q, k, v, kept, kbar, vbar, n_k, 1, b, 1 / math.sqrt(q.shape[2]), True, q_blocks=blocks)
+    order = np.random.default_rng(seed).permutation(geo.nqb).tolist()
+    done = []
+    while order and time.perf_counter() - t2 < budget_s:
+        batch, order = sorted(order[:8]), order[8:]
+        A.attend(q, k, v, kept, kbar, vbar, n_k, 1, b, 1 / math.sqrt(q.shape[2]), True, q_blocks=batch)
+        done += batch
     t3 = time.perf_counter()
     # attention work of a query block grows with its kept count; scale the
     # sampled time by total kept blocks / sampled kept blocks
     kept_rows = kept.sum(axis=2)[0]
-    scale_attn = kept_rows.sum() / kept_rows[blocks].sum()
+    scale_attn = kept_rows.sum() / kept_rows[done].sum()
     per_layer = hkv * ((t2 - t1) + (t3 - t2) * scale_attn)
-    return dict(value=per_layer * 1e3, unit="ms/layer (extrapolated)", cores=threads, kind="oracle",
+    return dict(value=round(float(per_layer) * 1e3, 1), unit="ms/layer (extrapolated)", cores=threads, kind="oracle",
                 sample=f"float64 oracle on KV group 0: pool+select over all {geo.nqb} query blocks "
-                       f"({t2 - t1:.1f} s) + attention of query blocks {blocks} ({t3 - t2:.1f} s); "
-                       f"extrapolated x{hkv} groups and by kept-block count",
+                       f"({t2 - t1:.1f} s) + attention of {len(done)} seeded random query blocks "
+                       f"({t3 - t2:.1f} s, {kept_rows[done].sum()} of {kept_rows.sum()} kept blocks); "
+                       f"extrapolated x{hkv} KV groups and by kept-block count",
                 measured_s=round(t3 - t1, 2))
+
+
+def timed(stream, fns, steps, warmup):
+    """Run the closures fns in order `steps` times after `warmup` untimed
+    rounds; HIP events on `stream` bracket each closure.  Returns the mean ms of
+    each closure, the mean ms of the whole round and the wall ms per round."""
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for row in ev:
+        row[0].record(stream)
+        for f, e in zip(fns, row[1:]):
+            f()
+            e.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [float(np.mean([row[j].elapsed_time(row[j + 1]) for row in ev])) for j in range(len(fns))]
+    total = float(np.mean([row[0].elapsed_time(row[-1]) for row in ev]))
+    return per, total, wall
+
+
+class ContigLayer:
+    """Device buffers and C-ABI closures of one contiguous (batch 1) layer."""
+
+    def __init__(self, fp2, q, k, v, p, S, hkv, d, b):
+        import torch
+        dev = q.device
+        self.fp2, self.q, self.k, self.v, self.p, self.S = fp2, q, k, v, p, S
+        nqb, nkb = fp2.fp2_num_q_blocks(S, S, b), fp2.fp2_num_k_blocks(S, b)
+        self.idx = torch.empty((1, hkv, nqb, nkb), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((1, hkv, nqb), dtype=torch.int32, device=dev)
+        self.pk = torch.empty((1, hkv, nkb, d), dtype=torch.float32, device=dev)
+        self.pv = torch.empty_like(self.pk)
+        self.ws = torch.empty(fp2.fp2_select_workspace_size(p, 1, S, S), dtype=torch.uint8, device=dev)
+        self.out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        self.out_d = None
+        self.sh = torch.cuda.current_stream().cuda_stream
+
+    def select(self):
+        f, S = self.fp2, self.S
+        st = f.fp2_select_blocks(self.p, 1, S, S, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                 self.idx.data_ptr(), self.cnt.data_ptr(), self.pk.data_ptr(), self.pv.data_ptr(),
+                                 self.ws.data_ptr(), self.ws.numel(), self.sh)
+        assert st == 0, f.last_error()
+
+    def attend(self):
+        f, S = self.fp2, self.S
+        st = f.fp2_sparse_prefill(self.p, 1, S, S, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                  self.idx.data_ptr(), self.cnt.data_ptr(), self.pk.data_ptr(), self.pv.data_ptr(),
+                                  self.out.data_ptr(), None, self.sh)
+        assert st == 0, f.last_error()
+
+    def dense(self):
+        import torch
+        f, S = self.fp2, self.S
+        if self.out_d is None:
+            self.out_d = torch.empty_like(self.out)
+        st = f.fp2_dense_prefill(self.p, 1, S, S, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                 self.out_d.data_ptr(), None, self.sh)
+        assert st == 0, f.last_error()
+
+    def sparse_vs_dense(self):
+        a, d = self.out.float(), self.out_d.float()
+        return round(float((a - d).norm() / d.norm()), 4)
+
+
+def fp8_legs(fp2, prob, hq, hkv, d, b, S, steps, warmup, dense_steps, stream, taus):
+    """FP8 variant of the 128K layer at each (sparsity, tau) in taus."""
+    import synth
+    import torch
+    dev = torch.device("cuda:0")
+    qc, qs = synth.quantize_e4m3(prob.q, 1)
+    kc, ks = synth.quantize_e4m3(prob.k, 1)
+    vc, vs = synth.quantize_e4m3(prob.v, 1)
+    q8, k8, v8, qs, ks, vs = (t.to(dev) for t in (qc, kc, vc, qs, ks, vs))
+    res = {}
+    p_dense = fp2.make_params(hq, hkv, d, b, fp8=True, q_scale=qs, k_scale=ks, v_scale=vs)
+    L = ContigLayer(fp2, q8, k8, v8, p_dense, S, hkv, d, b)
+    (dense_ms,), _, _ = timed(stream, [L.dense], dense_steps, 1)
+    F0 = None
+    for sp, tau in taus:
+        L.p = fp2.make_params(hq, hkv, d, b, tau=tau, fp8=True, q_scale=qs, k_scale=ks, v_scale=vs)
+        (sel, att), step, wall = timed(stream, [L.select, L.attend], steps, warmup)
+        F = flops(L.cnt.cpu().numpy(), hq, hkv, d, b, S)
+        F0 = F
+        ach = F["executed"] / att / 1e9
+        res[f"{sp:.2f}"] = dict(tau=round(tau, 5), ms=round(step, 3), select_ms=round(sel, 3),
+                                sparse_attn_ms=round(att, 3), block_sparsity=round(F["sparsity"], 4),
+                                eff_tflops_executed_attn=round(ach, 1),
+                                frac_fp8_peak=round(ach / PEAK_FP8_TFLOPS, 4),
+                                eff_tflops_dense_equiv=round(F["dense_eq"] / step / 1e9, 1),
+                                speedup_vs_fp8_dense=round(dense_ms / step, 2),
+                                sparse_vs_dense_rel_l2=L.sparse_vs_dense())
+        log(f"[bench] fp8 @{sp:.2f}: step {step:.3f} ms (select {sel:.3f}, attention {att:.3f}), "
+            f"sparsity {F['sparsity']:.4f}, {dense_ms / step:.2f}x vs fp8 dense")
+    dense = dict(ms=round(dense_ms, 3), tflops=round(F0["dense_exec"] / dense_ms / 1e9, 1),
+                 frac_fp8_peak=round(F0["dense_exec"] / dense_ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+    log(f"[bench] fp8 dense {dense_ms:.3f} ms")
+    return dict(levels=res, dense=dense, dtype="fp8 e4m3 (per-head scales), bf16 out")
+
+
+def paged_leg(fp2, w, tau, steps, warmup, stream, seed):
+    """The paged-KV continuous batch: one fp2_sparse_prefill_paged call."""
+    import synth
+    import torch
+    dev = torch.device("cuda:0")
+    hq, hkv, d, b = w["hq"], w["hkv"], w["d"], w["block"]
+    kv_lens, q_lens = w["kv_lens"], w["q_lens"]
+    t0 = time.time()
+    pb = synth.make_paged(seed, kv_lens, q_lens, hq, hkv, d, b, page_size=w["page_size"])
+    log(f"[bench] generated paged batch in {time.time() - t0:.1f}s")
+    p = fp2.make_params(hq, hkv, d, b, tau=tau)
+    q, cu, sk = pb.q.to(dev), pb.cu_seqlens_q.to(dev), pb.seqlens_k.to(dev)
+    kc, vc, tab = pb.k_cache.to(dev), pb.v_cache.to(dev), pb.page_table.to(dev)
+    n, msq, msk = len(kv_lens), max(q_lens), max(kv_lens)
+    mq, mk = fp2.fp2_paged_mask_dims(p, msq, msk)
+    idx = torch.empty((n, hkv, mq, mk), dtype=torch.int32, device=dev)
+    cnt = torch.empty((n, hkv, mq), dtype=torch.int32, device=dev)
+    ws = torch.empty(fp2.fp2_paged_workspace_size(p, n, msq, msk), dtype=torch.uint8, device=dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    sh = stream.cuda_stream
+
+    def run():
+        st = fp2.fp2_sparse_prefill_paged(p, n, q.data_ptr(), cu.data_ptr(), sk.data_ptr(), msq, msk, kc.data_ptr(),
+                                          vc.data_ptr(), kc.shape[0], kc.shape[1], tab.data_ptr(), tab.shape[1],
+                                          out.data_ptr(), None, idx.data_ptr(), cnt.data_ptr(), ws.data_ptr(),
+                                          ws.numel(), sh)
+        assert st == 0, fp2.last_error()
+
+    (ms,), _, wall = timed(stream, [run], steps, warmup)
+    c = cnt.cpu().numpy()
+    kept = vis = 0
+    executed = 0.0
+    G = hq // hkv
+    for s_, (L, Lq) in enumerate(zip(kv_lens, q_lens)):
+        first = (L - Lq) // b
+        nqb = (L - 1) // b - first + 1
+        kept_s = int(c[s_, :, :nqb].sum())
+        vis_s = hkv * sum(first + il + 1 for il in range(nqb))
+        kept += kept_s
+        vis += vis_s
+        executed += 4.0 * d * (G * b) * b * kept_s + 4.0 * d * (G * b) * (vis_s - kept_s)
+    ach = executed / ms / 1e9
+    log(f"[bench] paged batch6: {ms:.3f} ms, sparsity {1 - kept / vis:.4f}, {ach:.0f} TFLOP/s executed")
+    return dict(ms=round(ms, 3), wall_ms=round(wall, 3), tau=round(tau, 5), block_sparsity=round(1 - kept / vis, 4),
+                new_tokens=int(sum(q_lens)), cached_tokens=int(sum(kv_lens)),
+                eff_tflops_executed=round(ach, 1), frac_bf16_peak=round(ach / PEAK_BF16_TFLOPS, 4),
+                note="select + attention in one call (pool, score, select, attend over 64-token permuted pages)")
 
 
 def main():
@@ -123,6 +283,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), the reference for scaling "
@@ -148,83 +310,48 @@ def main():
     from tests.helpers import tau_table
 
     fp2.load()
+    taus = tau_table()
     w = synth.WORKLOADS[WORKLOAD]
     S, hq, hkv, d, b = w["seqlen"], w["hq"], w["hkv"], w["d"], w["block"]
-    tau = tau_table()[f"{WORKLOAD}@{w['sparsity']:.2f}"]["tau"]
+    tau = taus[f"{WORKLOAD}@{w['sparsity']:.2f}"]["tau"]
     t0 = time.time()
     prob = synth.make_problem(w["kind"], args.seed, S, hq, hkv, d, b)
     log(f"[bench] generated {WORKLOAD} in {time.time() - t0:.1f}s; tau={tau:.4f}")
 
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
     q, k, v = (t.to(dev) for t in (prob.q, prob.k, prob.v))
     p = fp2.make_params(hq, hkv, d, b, tau=tau)
-    nqb, nkb = fp2.fp2_num_q_blocks(S, S, b), fp2.fp2_num_k_blocks(S, b)
-    idx = torch.empty((1, hkv, nqb, nkb), dtype=torch.int32, device=dev)
-    cnt = torch.empty((1, hkv, nqb), dtype=torch.int32, device=dev)
-    pk = torch.empty((1, hkv, nkb, d), dtype=torch.float32, device=dev)
-    pv = torch.empty_like(pk)
-    ws = torch.empty(fp2.fp2_select_workspace_size(p, 1, S, S), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-
-    def select():
-        st = fp2.fp2_select_blocks(p, 1, S, S, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
-                                   cnt.data_ptr(), pk.data_ptr(), pv.data_ptr(), ws.data_ptr(), ws.numel(), sh)
-        assert st == 0, fp2.last_error()
-
-    def attend():
-        st = fp2.fp2_sparse_prefill(p, 1, S, S, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
-                                    cnt.data_ptr(), pk.data_ptr(), pv.data_ptr(), out.data_ptr(), None, sh)
-        assert st == 0, fp2.last_error()
-
-    for _ in range(args.warmup):
-        select()
-        attend()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        select()
-        e1.record(stream)
-        attend()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    sel_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
-    att_ms = float(np.mean([e1.elapsed_time(e2) for _, e1, e2 in ev]))
-    step_ms = float(np.mean([e0.elapsed_time(e2) for e0, _, e2 in ev]))
+    L = ContigLayer(fp2, q, k, v, p, S, hkv, d, b)
+    (sel_ms, att_ms), step_ms, wall_ms = timed(stream, [L.select, L.attend], args.steps, args.warmup)
     log(f"[bench] select {sel_ms:.3f} ms, attention {att_ms:.3f} ms, step {step_ms:.3f} ms (wall {wall_ms:.3f})")
 
-    F = flops(cnt.cpu().numpy(), hq, hkv, d, b, S)
+    F = flops(L.cnt.cpu().numpy(), hq, hkv, d, b, S)
     res_dense = None
     if not args.no_dense:
-        out_d = torch.empty_like(q)
-
-        def dense():
-            st = fp2.fp2_dense_prefill(p, 1, S, S, q.data_ptr(), k.data_ptr(), v.data_ptr(), out_d.data_ptr(), None,
-                                       sh)
-            assert st == 0, fp2.last_error()
-        dense()
-        torch.cuda.synchronize()
-        evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.dense_steps)]
-        for a_, b_ in evd:
-            a_.record(stream)
-            dense()
-            b_.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in evd]))
+        (dense_ms,), _, _ = timed(stream, [L.dense], args.dense_steps, 1)
         res_dense = dict(ms=round(dense_ms, 3), tflops=round(F["dense_exec"] / dense_ms / 1e9, 1),
-                         frac_peak=round(F["dense_exec"] / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 4))
+                         frac_peak=round(F["dense_exec"] / dense_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                         sparse_vs_dense_rel_l2=L.sparse_vs_dense())
         log(f"[bench] dense {dense_ms:.3f} ms")
-        diff = (out_d.float() - out.float()).norm() / out_d.float().norm()
-        res_dense["sparse_vs_dense_rel_l2"] = round(float(diff), 4)
-
     achieved = F["executed"] / att_ms / 1e9   # TFLOP/s
+    del L, q, k, v
+    torch.cuda.empty_cache()
+
+    res_fp8 = None
+    if not args.no_fp8:
+        wf = synth.WORKLOADS["llama8b_s128k_fp8"]
+        levels = [(sp, taus[f"llama8b_s128k_fp8@{sp:.2f}"]["tau"]) for sp in wf["sparsity"]]
+        res_fp8 = fp8_legs(fp2, prob, hq, hkv, d, b, S, args.steps, args.warmup, args.dense_steps, stream, levels)
+        torch.cuda.empty_cache()
+
+    res_paged = None
+    if not args.no_paged:
+        wp = synth.WORKLOADS["paged_batch6"]
+        res_paged = paged_leg(fp2, wp, taus[f"paged_batch6@{wp['sparsity']:.2f}"]["tau"], args.steps,
+                              args.warmup, stream, args.seed)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the float64 oracle on a bounded sample ...")
@@ -249,7 +376,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "attn_kernel<128,128> (fp2_sparse_prefill)"},
+                     "kernel": "attn_kernel<128,128,bf16> (fp2_sparse_prefill)"},
         "cpu_baseline": cpu,
         "breakdown": {
             "select_ms": round(sel_ms, 3),
@@ -263,6 +390,8 @@ def main():
             "eff_tflops_executed_attn": round(achieved, 1),
             "dense": res_dense,
             "speedup_vs_dense": round(res_dense["ms"] / step_ms, 2) if res_dense else None,
+            "fp8_128k": res_fp8,
+            "paged_batch6": res_paged,
             "kernel_source_hash": kernel_source_hash(),
         },
     }
