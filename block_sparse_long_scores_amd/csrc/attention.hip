@@ -44,6 +44,7 @@
 #include "fp2_internal.h"
 #include "geometry.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace fp2 {
@@ -132,11 +133,12 @@ __device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[4], const bf16x8 (&
   return S;
 }
 
+// One tile: the G*b packed query rows of (sequence, KV head, query block) or
+// the 256-row part `part` of them, over its kept key blocks (or all blocks
+// j <= i when dense), then the mean correction and the epilogue.
 template <int D, int BLK, bool F8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, char* smem) {
   using C = Cfg<D, BLK, F8>;
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int nwaves = nthr >> 6;
@@ -147,12 +149,11 @@ void attn_kernel(AttnArgs a) {
 
   // ---- tile.  Query blocks go from the last (longest) down; the G2 =
   // Hkv*batch*parts tiles of one query block are rotated by the query-block
-  // rank, so that under the round-robin workgroup -> XCD dispatch each XCD
-  // serves every head in turn (kept-block counts differ between heads) while
-  // the parts of one tile stay on the same XCD.
+  // rank, so that the XCD queue tile % 8 serves every head in turn (kept-block
+  // counts differ between heads) while the parts of one tile share a queue.
   const int G2 = a.Hkv * a.seq.batch * a.parts;
-  const int rank = blockIdx.x / G2;
-  int t = (blockIdx.x - rank * G2 + rank) % G2;
+  const int rank = tile / G2;
+  int t = (tile - rank * G2 + rank) % G2;
   const int h = t % a.Hkv;
   t /= a.Hkv;
   const int s = t % a.seq.batch;
@@ -795,6 +796,62 @@ void attn_kernel(AttnArgs a) {
   }
 }
 
+// Persistent tile scheduler.  The tiles t = 0 .. ntiles-1 (longest first)
+// form 8 queues, queue q = {t : t % 8 == q}, one per XCD under the
+// round-robin workgroup -> XCD dispatch; the gridDim.x <= #CU workgroups stay
+// resident, workgroup w starts with tile w of its home queue w % 8 and then
+// pulls the next position of its queue from a device-scope counter, moving
+// on to the other queues in turn once its own is drained.  Workgroups never
+// wait for the hardware dispatcher between tiles (with tiles of very
+// different lengths that dispatcher leaves CUs idle), while the two parts of
+// one tile and the tiles of one head in a query-block rank stay in one XCD's
+// L2.  g_sched holds one set of 8 counters (each on its own 128-byte line)
+// per launch slot; the launcher zeroes the slot's counters with
+// sched_reset_kernel on the same stream right before the launch, and hands
+// out slots round-robin so that launches running concurrently on different
+// streams use different counters.
+constexpr int kSchedSlots = 64;
+__device__ unsigned int g_sched[kSchedSlots][8][32];
+
+__global__ void sched_reset_kernel(int slot) {
+  if (threadIdx.x < 8) atomicExch(&g_sched[slot][threadIdx.x][0], 0u);
+}
+
+template <int D, int BLK, bool F8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int nwg = gridDim.x;
+  const int home = blockIdx.x & 7;
+  unsigned int(*ctr)[32] = g_sched[a.sched_slot];
+  // next-tile broadcast, double-buffered: the slot written at iteration k is
+  // rewritten at k+2, after every thread has passed the barrier of k+1
+  volatile int* next_slot = (volatile int*)(smem + a.lds_sched);
+  int tile = blockIdx.x;
+  int qi = 0;        // thread 0: queues drained so far
+  unsigned pre = 0;  // thread 0: position fetched from queue (home + qi) % 8
+  for (int k = 0;; ++k) {
+    if (threadIdx.x == 0 && qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
+    attn_tile<D, BLK, F8>(a, tile, smem);
+    if (threadIdx.x == 0) {
+      int nxt = -1;
+      while (qi < 8) {
+        const int q = (home + qi) & 7;
+        const int pos = (nwg - q + 7) / 8 + (int)pre;  // the home workgroups took positions [0, nhome)
+        if (8 * pos + q < a.ntiles) {
+          nxt = 8 * pos + q;
+          break;
+        }
+        if (++qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
+      }
+      next_slot[k & 1] = nxt;
+    }
+    __syncthreads();
+    tile = __builtin_amdgcn_readfirstlane(next_slot[k & 1]);
+    if (tile < 0) break;
+  }
+}
+
 // LDS bytes the attention kernel needs for a given key-block count.
 template <int D, int BLK, bool F8>
 static size_t attn_lds_bytes(int nkb) {
@@ -804,16 +861,41 @@ static size_t attn_lds_bytes(int nkb) {
   return corr > lds ? corr : lds;
 }
 
+static int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev >= 64) dev = 63;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+static std::atomic<unsigned> g_slot_counter{0};
+
 template <int D, int BLK, bool F8>
-static hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-  const long nwg = (long)a.Hkv * a.seq.batch * a.parts * a.nqb_grid;
-  const size_t lds = attn_lds_bytes<D, BLK, F8>(a.seq.nkb_stride);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
+  const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
+  const size_t lds = attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
+  const size_t lds_total = lds + 16;  // + the next-tile broadcast slots
+  if (lds_total > 160 * 1024) return hipErrorInvalidValue;
+  if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_total);
   if (e != hipSuccess) return e;
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, BLK, F8>), dim3((unsigned)nwg), dim3(64 * a.waves), lds, st, a);
+  if (ntiles == 0) return hipSuccess;
+  AttnArgs a = a0;
+  a.ntiles = (int)ntiles;
+  a.sched_slot = (int)(g_slot_counter.fetch_add(1) % kSchedSlots);
+  a.lds_sched = (int)lds;
+  const long grid = ntiles < compute_units() ? ntiles : compute_units();
+  hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, st, a.sched_slot);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_kernel<D, BLK, F8>), dim3((unsigned)grid), dim3(64 * a.waves), lds_total, st, a);
   return hipGetLastError();
 }
 

@@ -75,7 +75,11 @@ struct AttnArgs {
   int out_fp32;
   int parts;                // workgroups per (seq, head, q-block) tile
   int waves;                // waves per workgroup
-  int nqb_grid;             // query-block extent of the grid
+  int nqb_grid;             // query-block extent of the tile space
+  // set by the launcher
+  int ntiles;               // Hkv * batch * parts * nqb_grid
+  int sched_slot;           // tile-scheduler counter slot of this launch
+  int lds_sched;            // LDS byte offset of the next-tile broadcast
 };
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
