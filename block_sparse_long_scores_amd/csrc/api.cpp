@@ -303,9 +303,10 @@ fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const
     return fail(FP2_EINVAL, "q, cu_seqlens_q, seqlens_k, k_cache, v_cache, page_table and out must be non-NULL");
   if ((block_idx == nullptr) != (block_cnt == nullptr))
     return fail(FP2_EINVAL, "block_idx and block_cnt must be both NULL or both set");
-  if (page_size <= 0 || (page_size & (page_size - 1)) || p->block_size % page_size)
-    return fail(FP2_EUNSUPPORTED, "page_size=%d must be a power of two dividing block_size=%d", page_size,
-                p->block_size);
+  if (page_size <= 0 || (page_size & (page_size - 1)) || p->block_size % page_size ||
+      p->block_size / page_size > 64)
+    return fail(FP2_EUNSUPPORTED, "page_size=%d must be a power of two dividing block_size=%d, at least %d",
+                page_size, p->block_size, p->block_size / 64);
   if (num_pages <= 0) return fail(FP2_EINVAL, "num_pages=%d must be positive", num_pages);
   const int b = p->block_size, D = p->head_dim;
   if ((long)max_pages_per_seq * page_size < max_seqlen_k)

@@ -230,46 +230,80 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
   const int plog = a.kv.page_log2;
   const int* ptab = a.kv.page_table ? a.kv.page_table + (long)s * a.kv.max_pages : nullptr;
 
+  // Paged caches: page ids of key block j, lane i holding the id of its i-th
+  // page (a block spans BLK / page_size <= 64 pages; page_size divides BLK).
+  // They are loaded one block ahead of the K/V copies that use them, so that
+  // no copy address waits on a load (vmcnt drains in order: a wait for the
+  // page table would also wait for every copy already in flight).
+  auto load_pids = [&](int j) __attribute__((always_inline)) -> int {
+    if (!ptab) return 0;
+    const int p0 = (j * BLK) >> plog;
+    const int npg = max(1, BLK >> plog);
+    return lane < npg ? ptab[min(p0 + lane, Skm1 >> plog)] : 0;
+  };
+
   // K and V tile of key block j -> LDS buffer bb (async, global_load_lds).
-  // Wave op `it` fills tile bytes [1024*it, 1024*it + 1024); lane bytes that
-  // fall into a row pad (or past the last row) reload chunk 0 of a valid row.
-  // Paged caches: the rows of one wave op span at most two pages when a page
-  // holds 16 rows or more; their two page ids are wave-uniform loads, so no
-  // per-lane load has to complete before the copies are issued.
-  auto issue_load = [&](int j, int bb) __attribute__((always_inline)) {
-    const int kb0 = j * BLK;
-    for (int it = wave; it < C::NLD; it += nwaves) {
-      const int o = it * 1024 + lane * 16;
-      int row = o / C::RS;
-      const int w = o - row * C::RS;
-      int c = w < C::ROWB ? (w >> 4) : 0;
-      if (row >= BLK) {
-        row = BLK - 1;
-        c = 0;
-      }
-      const int key = min(kb0 + row, Skm1);
-      long rix;
-      if (ptab) {
-        int pg;
-        if (plog >= 4) {
-          const int klo = min(kb0 + (it * 1024) / C::RS, Skm1);
-          const int khi = min(kb0 + min((it * 1024 + 1023) / C::RS, BLK - 1), Skm1);
-          const int plo = ptab[klo >> plog];
-          const int phi = ptab[khi >> plog];
-          pg = (key >> plog) == (klo >> plog) ? plo : phi;
-        } else {
-          pg = ptab[key >> plog];
-        }
-        rix = ((long)pg << plog) + (key & ((1 << plog) - 1));
-      } else {
-        rix = (long)s * a.seq.seqlen_k + key;
-      }
-      const long boff = rix * rowbytes + h * C::ROWB + c * 16;
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)a.kv.k + boff),
-                                       (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)a.kv.v + boff),
-                                       (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024), 16, 0, 0);
+  // Wave op `it` (it = wave, wave + nwaves, ...) fills tile bytes [1024*it,
+  // 1024*it + 1024) with 16 bytes per lane: lane bytes o = 1024*it + 16*lane
+  // fall in row o / RS at byte o % RS; bytes in a row pad (or past the last
+  // row) reload chunk 0 of a valid row.  The (row, byte) pair of each lane is
+  // advanced by a fixed step per op instead of being divided out; the copy
+  // address is a wave-uniform block base plus a 32-bit lane offset; rows past
+  // the last key reload the last key.  The copies go through a cursor
+  // (dma_begin, then dma_step per op); run_tile can advance it by `dq` ops
+  // per chunk (0 everywhere now: interleaving the copies of the next block
+  // with the compute measured slower than issuing them before it).
+  const int step = 1024 * nwaves;
+  const int drow = step / C::RS, dbyte = step - drow * C::RS;
+  const int o0 = 1024 * wave + 16 * lane;
+  const int row0 = o0 / C::RS, byte0 = o0 - row0 * C::RS;
+  int dq_it = C::NLD, dq_row = 0, dq_byte = 0, dq_kb0 = 0, dq_rlast = 0, dq_bb = 0, dq_pids = 0;
+  const char* dq_kp = nullptr;
+  const char* dq_vp = nullptr;
+  auto dma_begin = [&](int j, int bb, int pids) __attribute__((always_inline)) {
+    dq_kb0 = j * BLK;
+    dq_rlast = min(Skm1 - dq_kb0, BLK - 1);  // last row holding a key of this block
+    dq_row = row0;
+    dq_byte = byte0;
+    dq_it = wave;
+    dq_bb = bb;
+    dq_pids = pids;
+    const long b0 = ptab ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + dq_kb0) * rowbytes + h * C::ROWB;
+    dq_kp = (const char*)a.kv.k + b0;
+    dq_vp = (const char*)a.kv.v + b0;
+  };
+  auto dma_step = [&]() __attribute__((always_inline)) {
+    if (dq_it >= C::NLD) return;
+    const bool inrow = dq_byte < C::ROWB && dq_row <= dq_rlast;
+    long off;
+    if (!ptab) {
+      off = (unsigned)(min(dq_row, dq_rlast) * rowbytes + (inrow ? dq_byte : 0));
+    } else {
+      const int key = dq_kb0 + min(dq_row, dq_rlast);
+      const int pg = __builtin_amdgcn_ds_bpermute(((key >> plog) - (dq_kb0 >> plog)) << 2, dq_pids);
+      off = (((long)pg << plog) + (key & ((1 << plog) - 1))) * rowbytes + (inrow ? dq_byte : 0);
     }
+    __builtin_amdgcn_global_load_lds((const void*)(dq_kp + off), (lds_void*)(lds + dq_bb * C::TILE + dq_it * 1024),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(dq_vp + off),
+                                     (lds_void*)(lds + (2 + dq_bb) * C::TILE + dq_it * 1024), 16, 0, 0);
+    dq_it += nwaves;
+    dq_row += drow;
+    dq_byte += dbyte;
+    if (dq_byte >= C::RS) {
+      dq_byte -= C::RS;
+      dq_row += 1;
+    }
+  };
+  auto dma_some = [&](int n) __attribute__((always_inline)) {
+    for (int k = 0; k < n; ++k) dma_step();
+  };
+  auto dma_rest = [&]() __attribute__((always_inline)) {
+    while (dq_it < C::NLD) dma_step();
+  };
+  auto issue_load = [&](int j, int bb, int pids) __attribute__((always_inline)) {
+    dma_begin(j, bb, pids);
+    dma_rest();
   };
 
   // ===================== bf16 operand path (32x32x16 MFMA) =================
@@ -359,7 +393,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
   // tile base offsets go through readfirstlane so every LDS operand address
   // is one base register plus a 16-bit immediate.
   auto run_tile = [&](const char* kt, const char* vt, int nch, int mode, int nvalid, float bias,
-                      const bf16x8 (&qq)[NT][C::KS]) __attribute__((always_inline)) {
+                      const bf16x8 (&qq)[NT][C::KS], int dq) __attribute__((always_inline)) {
     const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
     const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
     const char* kbase = lds + kbo;
@@ -378,6 +412,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
       const int cp = c & 1, np = cp ^ 1;
       const bool more = c + 1 < nch;
       if (more) load_kop(kbase, c + 1, kop);
+      dma_some(dq);
       // stage 1
       softmax(S[cp][0], 0, c, mode, nvalid, bias, p0);
       if (more) S[np][0] = qk(kop, qq[0]);
@@ -498,7 +533,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
   // 64-key steps:
   //   stage A: softmax(S_sc, columns 0) || QK(sc+1, columns 0), PV(sc-1, columns 1)
   //   stage B: softmax(S_sc, columns 1) || QK(sc+1, columns 1), PV(sc, columns 0)
-  auto run_tile8 = [&](const char* kt, const char* vt, int mode) __attribute__((always_inline)) {
+  auto run_tile8 = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
     const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
     const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
     const char* kbase = lds + kbo;
@@ -524,6 +559,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
         load_kop8(kbase, 2 * sc + 2, kop[0]);
         load_kop8(kbase, 2 * sc + 3, kop[1]);
       }
+      dma_some(dq);
       // stage A
       softmax8(S[cp][0], 0, sc, mode, pp0, sb0);
       if (more) {
@@ -548,13 +584,15 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
     pv8(vop[lp], pp1[lp], sb1[lp], 1);
   };
 
-  auto run_main = [&](const char* kt, const char* vt, int mode) __attribute__((always_inline)) {
+  // dq: next-block copy ops to issue per chunk (per superchunk in fp8)
+  auto run_main = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
     if constexpr (F8) {
-      run_tile8(kt, vt, mode);
+      run_tile8(kt, vt, mode, dq);
     } else {
-      run_tile(kt, vt, C::KC, mode, 0, 0.f, qop);
+      run_tile(kt, vt, C::KC, mode, 0, 0.f, qop, dq);
     }
   };
+
 
   // ---- kept blocks (sparse) or all blocks j <= i (dense)
   const long mrow = ((long)s * a.Hkv + h) * a.seq.nqb_stride + il;
@@ -564,7 +602,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
 
   // Reference max per query row: max logit over the first 32 keys of the
   // first block (causally masked if that block is the diagonal), + margin.
-  issue_load(j0, 0);
+  issue_load(j0, 0, load_pids(j0));
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   {
@@ -607,22 +645,29 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
     }
     if (pass > 0) {
       __syncthreads();
-      issue_load(j0, 0);
+      issue_load(j0, 0, load_pids(j0));
     }
     // Blocks 0 .. nblk-2 are strictly below the diagonal (the list is
     // ascending and ends with block i): one unmasked loop, the diagonal block
     // peeled after it.  List entries are read two blocks ahead so that the
     // address of the next K/V prefetch never waits on memory.
+    // Paged: the page ids of the block after next are loaded together with
+    // the copies of the next block.
     int jnext = nblk > 1 ? (a.sparse ? list[1] : 1) : 0;
+    int jafter = nblk > 2 ? (a.sparse ? list[2] : 2) : 0;
+    int pnext = load_pids(jnext);
     for (int n = 0; n + 1 < nblk; ++n) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const int jafter = n + 2 < nblk ? (a.sparse ? list[n + 2] : n + 2) : 0;
-      issue_load(jnext, (n + 1) & 1);
+      const int jafter2 = n + 3 < nblk ? (a.sparse ? list[n + 3] : n + 3) : 0;
+      const int pafter = load_pids(jafter);
+      issue_load(jnext, (n + 1) & 1, pnext);
       const char* kt = lds + (n & 1) * C::TILE;
       const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      run_main(kt, vt, 0);
+      run_main(kt, vt, 0, 0);
       jnext = jafter;
+      jafter = jafter2;
+      pnext = pafter;
     }
     {
       const int n = nblk - 1;
@@ -630,7 +675,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
       __syncthreads();
       const char* kt = lds + (n & 1) * C::TILE;
       const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      run_main(kt, vt, 1);
+      run_main(kt, vt, 1, 0);
     }
 
     // ---- mean correction: dropped blocks as pseudo-keys
@@ -732,9 +777,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
         }
         __syncthreads();
         if constexpr (F8) {
-          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, q16);
+          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, q16, 0);
         } else {
-          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, qop);
+          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, qop, 0);
         }
       }
     }

@@ -149,7 +149,8 @@ fp2_status fp2_dense_prefill(const fp2_params* p, int32_t batch,
  *                  query row r sits at position seqlens_k[s] - q_len + r.
  *   max_seqlen_q, max_seqlen_k : host upper bounds of q_len and seqlens_k.
  *   k_cache, v_cache : [num_pages, page_size, Hkv, d] (in_dtype).
- *   page_size    : must divide block_size.
+ *   page_size    : a power of two dividing block_size, at least
+ *                  block_size / 64 (a block spans at most 64 pages).
  *   page_table   : int32 [num_seqs, max_pages_per_seq] device; token t of
  *                  sequence s lives in page page_table[s][t / page_size], row
  *                  t % page_size.  Entries must be in [0, num_pages); with

@@ -98,6 +98,7 @@ def test_paged_validation_errors():
                                             a["idx"], a["cnt"], a["ws"], a["wsb"], None)
     assert call(page=48) == fp2.FP2_EUNSUPPORTED
     assert call(page=256) == fp2.FP2_EUNSUPPORTED           # must divide the block size
+    assert call(page=1) == fp2.FP2_EUNSUPPORTED             # a block spans at most 64 pages
     assert call(table=None) == fp2.FP2_EINVAL
     assert call(idx=FAKE) == fp2.FP2_EINVAL                 # idx without cnt
     assert call(mpp=8) == fp2.FP2_EINVAL                    # table too short for max_seqlen_k
