@@ -36,9 +36,18 @@ def sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+# Per-source code-generation options.  The bf16 attention kernel asks for the
+# VGPR form of the MFMA results (S then stays in VGPRs for the softmax instead
+# of being read back from AGPRs one value at a time); the fp8 one keeps the
+# default selection.
+EXTRA = {
+    "attention_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,977 +1,15 @@
-// Block-sparse (and dense) causal prefill attention with mean correction, gfx950.
-//
-// Source: "FlashPrefill V2: block-sparse prefill attention for long-context LLM
-// serving", abstract (sparse attention operator with PackGQA memory access,
-// FP8, paged KV cache, mean correction term), and the papers.ananclaw.com
-// explainer §2.1 (query block q computes only Supp(q); Out_q^V2 adds the
-// dropped blocks' mass through mu_q and their average value) and §2.2
-// (PackGQA).  The pages' kernel targets Hopper (warp specialization, pingpong);
-// this one is laid out for CDNA4 instead:
-//
-//  * One workgroup per (sequence, KV head h, query block i, part): its 4
-//    wavefronts hold 256 of the G query heads x b rows of the GQA group, 64
-//    packed query rows per wave (PackGQA: every query head of the group reads
-//    the same K/V tile from LDS; a 512-row group takes two workgroups, which
-//    land on the same XCD and share its L2).
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: keys on the M side, queries on
-//    the N side, so each lane owns 2 query columns and the row max / row sum
-//    of the online softmax are lane-local plus one permlane32 exchange.
-//  * The accumulator registers of S^T, in order, are the B-operand slots of
-//    the P V MFMA (4 consecutive keys per half-slot), so P^T feeds
-//    v_mfma_f32_32x32x16_bf16 straight from registers; O^T = V^T P^T
-//    accumulates in the AGPR file.  The V^T operand comes from
-//    ds_read_b64_tr_b16 (LDS transpose read: 4 consecutive keys of one d per
-//    lane) on the natural [key][d] tile.
-//  * K and V both travel HBM -> LDS with global_load_lds_dwordx4 (no register
-//    staging), double-buffered: block n+1 streams in while block n is
-//    computed.  LDS rows are padded (row + 32 B for d = 128) so that the
-//    operand reads are bank-conflict-free and every operand address is one
-//    base register plus a compile-time offset.
-//  * Softmax in the log2 domain against a fixed per-row reference m: before
-//    the block loop each query row takes the max of its logits over the first
-//    32 keys of its first kept block (the sink block) plus kRefMargin.  The
-//    loop then needs one FMA, one exp2, one add and half a convert per score
-//    and never rescales the AGPR-resident O^T.  m is at most kRefMargin above
-//    the row's true max, so the largest term keeps full precision; a row whose
-//    normaliser reaches 2^kRefOverflow (a logit ~80 nats above the sink chunk)
-//    makes the workgroup recompute the tile with m moved up by log2 of that
-//    normaliser, which bounds every term by 1 (exact, just slower).
-//  * Mean correction: after the kept blocks, the dropped blocks of the row
-//    (the complement of the kept list in [0, i)) are processed 32 at a time
-//    as pseudo-keys: K row = kbar_j, V row = vbar_j (bf16 in LDS), logit bias
-//    log2(n_j), no causal mask (dropped blocks lie strictly before i).
-#include "fp2_device.h"
+// Precision dispatch of the attention kernel (instantiated in attention_bf16.hip and
+// attention_fp8.hip, which are compiled with different code-generation options).
 #include "fp2_internal.h"
-#include "geometry.h"
-
-#include <atomic>
-#include <type_traits>
 
 namespace fp2 {
 
-constexpr int kRowsPerWave = 64;
-constexpr int kRowsPerPart = 256;
-constexpr int NT = kRowsPerWave / 32;  // 32-query column groups per wave
-constexpr float kRefMargin = 16.0f;     // log2 units above the sink-chunk max
-constexpr float kRefOverflow = 100.0f;  // log2 of the normaliser that forces a rerun
-constexpr int kMaxPasses = 4;
-
-template <int D, int BLK, bool F8>
-struct Cfg {
-  static constexpr int ESZ = F8 ? 1 : 2;       // bytes per K/V element
-  static constexpr int KS = D / 16;            // k-steps of a bf16 QK chain (32x32x16)
-  static constexpr int KS8 = D / 64;           // k-steps of an fp8 QK chain (32x32x64)
-  static constexpr int MT = D / 32;            // 32-row tiles of O^T along d
-  static constexpr int KC = BLK / 32;          // 32-key chunks per block
-  static constexpr int NSC = BLK / 64;         // 64-key superchunks per block (fp8 P V)
-  static constexpr int ROWB = D * ESZ;         // bytes of one K/V row of one head
-  // LDS row stride: rows are padded so that the rows read by one LDS read
-  // phase (consecutive rows for the K operand, the 4/8-key groups of the
-  // transpose reads for V) land on distinct banks.
-  static constexpr int RS = F8 ? ROWB + 16 : ROWB + (D == 128 ? 32 : 16);
-  static constexpr int TILE = ((BLK * RS + 1023) / 1024) * 1024;  // one K or V tile
-  static constexpr int NLD = TILE / 1024;      // global_load_lds wave ops per tile
-  static constexpr int RS16 = 2 * D + (D == 128 ? 32 : 16);  // bf16 pseudo-key rows
-  static constexpr int PSB = 32 * RS16;        // one 32-row pseudo-key tile (bf16)
-  static constexpr int STG = 2 * 32 * D * 4;   // fp32 kbar + vbar rows of one pseudo chunk
-};
-
-// Byte offset of the correction-phase staging buffers (after the pseudo tiles,
-// the count, the bitmap and the dropped list).
-template <int D, int BLK, bool F8>
-__host__ __device__ constexpr int corr_stage_offset(int nkb) {
-  return ((2 * Cfg<D, BLK, F8>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb + 1023) / 1024) * 1024;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
-// S^T chunk = sum_ks K_ks Q_ks^T as a chain of v_mfma_f32_32x32x16_bf16 whose
-// accumulator stays in VGPRs (the O^T accumulators own the AGPR file, and the
-// compiler would otherwise place S in AGPRs as well and spill).  Hazards the
-// compiler cannot see through the asm are covered inside it: 2 wait states
-// before the first MFMA (VALU write -> MFMA source read) and 20 after the last
-// (MFMA result -> VALU read); a dependent MFMA chain on the same accumulator
-// needs none.
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[8], const bf16x8 (&q)[8]) {
-  f32x16 S;
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %9, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %11, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %13, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %6, %14, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %15, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3"
-      : "=&v"(S)
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]),
-        "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
-  return S;
-}
-
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[4], const bf16x8 (&q)[4]) {
-  f32x16 S;
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3"
-      : "=&v"(S)
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
-  return S;
-}
-
-// One tile: the G*b packed query rows of (sequence, KV head, query block) or
-// the 256-row part `part` of them, over its kept key blocks (or all blocks
-// j <= i when dense), then the mean correction and the epilogue.
-template <int D, int BLK, bool F8>
-__device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, char* smem) {
-  using C = Cfg<D, BLK, F8>;
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
-  const int nwaves = nthr >> 6;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = lane >> 5;
-  const int l32 = lane & 31;
-
-  // ---- tile.  Query blocks go from the last (longest) down; the G2 =
-  // Hkv*batch*parts tiles of one query block are rotated by the query-block
-  // rank, so that the XCD queue tile % 8 serves every head in turn (kept-block
-  // counts differ between heads) while the parts of one tile share a queue.
-  const int G2 = a.Hkv * a.seq.batch * a.parts;
-  const int rank = tile / G2;
-  int t = (tile - rank * G2 + rank) % G2;
-  const int h = t % a.Hkv;
-  t /= a.Hkv;
-  const int s = t % a.seq.batch;
-  t /= a.seq.batch;
-  const int part = t;
-  const int il = a.nqb_grid - 1 - rank;
-  const SeqGeo g = seq_geo(a.seq, s, BLK);
-  if (il < 0 || il >= g.nqb) return;
-  const int i = g.first_qb + il;
-  const int G = a.G;
-  const int pr0 = part * kRowsPerPart + wave * kRowsPerWave;
-
-  // query column nt of this lane: packed row pr = pr0 + l32 + 32*nt, i.e.
-  // query head h*G + pr/BLK, row pr%BLK of block i.
-  auto qinfo = [&](int nt, int& rb, long& off) __attribute__((always_inline)) -> bool {
-    const int pr = pr0 + l32 + 32 * nt;
-    const int gq = pr / BLK;
-    rb = pr - gq * BLK;
-    const int r = i * BLK + rb - g.P;
-    off = ((long)(g.qrow0 + r) * a.Hq + (h * G + gq)) * D;
-    return (pr < G * BLK) && r >= 0 && r < g.Sq;
-  };
-
-  // Q operands (B side of S^T) and the log2-domain scale of a raw score.
-  //  bf16: k-step ks of lane (n, hh) holds d in [16ks + 8hh, +8).
-  //  fp8:  k-step ks of lane (n, hh) holds d in [64ks + 32hh, +32) (the
-  //        32x32x64 MFMA pairs byte e of A lane (x, hh) with byte e of B
-  //        lane (n, hh)); a raw score is in code units and takes the
-  //        per-head dequantization scales q_s * k_s.
-  using QT = typename std::conditional<F8, i32x8, bf16x8>::type;
-  constexpr int QKS = F8 ? C::KS8 : C::KS;
-  int rib[NT];
-  float cs[NT];
-  QT qop[NT][QKS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    long off;
-    const bool ok = qinfo(nt, rib[nt], off);
-    if constexpr (F8) {
-      const unsigned char* qp = (const unsigned char*)a.q + off + 32 * hh;
-#pragma unroll
-      for (int ks = 0; ks < QKS; ++ks) {
-        if (ok) {
-          const i32x4 lo = *(const i32x4*)(qp + 64 * ks);
-          const i32x4 hi = *(const i32x4*)(qp + 64 * ks + 16);
-          qop[nt][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        } else {
-          qop[nt][ks] = i32x8{};
-        }
-      }
-      const int gq = (pr0 + l32 + 32 * nt) / BLK;
-      cs[nt] = ok ? a.scale_log2 * a.q_scale[h * G + gq] * a.k_scale[h] : a.scale_log2;
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < QKS; ++ks) {
-        if (ok) {
-          qop[nt][ks] = *(const bf16x8*)((const __bf16*)a.q + off + 16 * ks + 8 * hh);
-        } else {
-          qop[nt][ks] = bf16x8{};
-        }
-      }
-      cs[nt] = a.scale_log2;
-    }
-  }
-
-  f32x16 O[C::MT][NT];
-  f32x16 Lacc[F8 ? NT : 1];  // fp8: row sums of P, accumulated by MFMA
-  float mref[NT], lsum[NT];
-
-  // LDS: K tiles at [0, 2*TILE), V tiles at [2*TILE, 4*TILE) (double buffer)
-  char* const lds = smem;
-  const int rowbytes = a.Hkv * C::ROWB;
-  const int Skm1 = g.Sk - 1;
-  const int plog = a.kv.page_log2;
-  const int* ptab = a.kv.page_table ? a.kv.page_table + (long)s * a.kv.max_pages : nullptr;
-
-  // Paged caches: page ids of key block j, lane i holding the id of its i-th
-  // page (a block spans BLK / page_size <= 64 pages; page_size divides BLK).
-  // They are loaded one block ahead of the K/V copies that use them, so that
-  // no copy address waits on a load (vmcnt drains in order: a wait for the
-  // page table would also wait for every copy already in flight).
-  auto load_pids = [&](int j) __attribute__((always_inline)) -> int {
-    if (!ptab) return 0;
-    const int p0 = (j * BLK) >> plog;
-    const int npg = max(1, BLK >> plog);
-    return lane < npg ? ptab[min(p0 + lane, Skm1 >> plog)] : 0;
-  };
-
-  // K and V tile of key block j -> LDS buffer bb (async, global_load_lds).
-  // Wave op `it` (it = wave, wave + nwaves, ...) fills tile bytes [1024*it,
-  // 1024*it + 1024) with 16 bytes per lane: lane bytes o = 1024*it + 16*lane
-  // fall in row o / RS at byte o % RS; bytes in a row pad (or past the last
-  // row) reload chunk 0 of a valid row.  The (row, byte) pair of each lane is
-  // advanced by a fixed step per op instead of being divided out; the copy
-  // address is a wave-uniform block base plus a 32-bit lane offset; rows past
-  // the last key reload the last key.  The copies go through a cursor
-  // (dma_begin, then dma_step per op); run_tile can advance it by `dq` ops
-  // per chunk (0 everywhere now: interleaving the copies of the next block
-  // with the compute measured slower than issuing them before it).
-  const int step = 1024 * nwaves;
-  const int drow = step / C::RS, dbyte = step - drow * C::RS;
-  const int o0 = 1024 * wave + 16 * lane;
-  const int row0 = o0 / C::RS, byte0 = o0 - row0 * C::RS;
-  int dq_it = C::NLD, dq_row = 0, dq_byte = 0, dq_kb0 = 0, dq_rlast = 0, dq_bb = 0, dq_pids = 0;
-  const char* dq_kp = nullptr;
-  const char* dq_vp = nullptr;
-  auto dma_begin = [&](int j, int bb, int pids) __attribute__((always_inline)) {
-    dq_kb0 = j * BLK;
-    dq_rlast = min(Skm1 - dq_kb0, BLK - 1);  // last row holding a key of this block
-    dq_row = row0;
-    dq_byte = byte0;
-    dq_it = wave;
-    dq_bb = bb;
-    dq_pids = pids;
-    const long b0 = ptab ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + dq_kb0) * rowbytes + h * C::ROWB;
-    dq_kp = (const char*)a.kv.k + b0;
-    dq_vp = (const char*)a.kv.v + b0;
-  };
-  auto dma_step = [&]() __attribute__((always_inline)) {
-    if (dq_it >= C::NLD) return;
-    const bool inrow = dq_byte < C::ROWB && dq_row <= dq_rlast;
-    long off;
-    if (!ptab) {
-      off = (unsigned)(min(dq_row, dq_rlast) * rowbytes + (inrow ? dq_byte : 0));
-    } else {
-      const int key = dq_kb0 + min(dq_row, dq_rlast);
-      const int pg = __builtin_amdgcn_ds_bpermute(((key >> plog) - (dq_kb0 >> plog)) << 2, dq_pids);
-      off = (((long)pg << plog) + (key & ((1 << plog) - 1))) * rowbytes + (inrow ? dq_byte : 0);
-    }
-    __builtin_amdgcn_global_load_lds((const void*)(dq_kp + off), (lds_void*)(lds + dq_bb * C::TILE + dq_it * 1024),
-                                     16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(dq_vp + off),
-                                     (lds_void*)(lds + (2 + dq_bb) * C::TILE + dq_it * 1024), 16, 0, 0);
-    dq_it += nwaves;
-    dq_row += drow;
-    dq_byte += dbyte;
-    if (dq_byte >= C::RS) {
-      dq_byte -= C::RS;
-      dq_row += 1;
-    }
-  };
-  auto dma_some = [&](int n) __attribute__((always_inline)) {
-    for (int k = 0; k < n; ++k) dma_step();
-  };
-  auto dma_rest = [&]() __attribute__((always_inline)) {
-    while (dq_it < C::NLD) dma_step();
-  };
-  auto issue_load = [&](int j, int bb, int pids) __attribute__((always_inline)) {
-    dma_begin(j, bb, pids);
-    dma_rest();
-  };
-
-  // ===================== bf16 operand path (32x32x16 MFMA) =================
-  // Used for the bf16 K/V tiles and, in both precisions, for the bf16
-  // pseudo-key tiles of the mean correction (row stride RS16).
-  //  K (A side of S^T): row l32 of the chunk; the d-range of k-step ks
-  //  matches the Q operand: bf16 Q [16ks + 8hh, +8); fp8 Q converted to bf16
-  //  [64(ks/4) + 32hh + 8(ks%4), +8).
-  //  V (A side of O^T, transpose read): group g = lane/16 reads rows
-  //  K0 + (lane%16)/4 at d = 32*mt + 16*(g%2) + 4*(lane%4), K0 = 16*ks2 +
-  //  8*sec + 4*hh within the chunk.
-  const int koff16 = l32 * C::RS16 + (F8 ? 64 : 16) * hh;
-  const int voff16 = (4 * hh + ((lane & 15) >> 2)) * C::RS16 + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-  auto kofs16 = [](int ks) constexpr -> int { return F8 ? 128 * (ks >> 2) + 16 * (ks & 3) : 32 * ks; };
-
-  auto load_kop = [&](const char* kt, int kc, bf16x8 (&kop)[C::KS]) __attribute__((always_inline)) {
-    const char* kb = kt + kc * 32 * C::RS16 + koff16;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kop[ks] = *(const bf16x8*)(kb + kofs16(ks));
-  };
-  auto load_vop = [&](const char* vt, int kc, bf16x8 (&vop)[C::MT][2]) __attribute__((always_inline)) {
-    const char* vb = vt + kc * 32 * C::RS16 + voff16;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + 16 * ks2 * C::RS16));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + (16 * ks2 + 8) * C::RS16));
-        vop[mt][ks2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
-  };
-  auto qk = [&](const bf16x8 (&kop)[C::KS], const bf16x8 (&qq)[C::KS]) __attribute__((always_inline)) -> f32x16 {
-    f32x16 S = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qq[ks], S, 0, 0, 0);
-    return S;
-  };
-  // P = exp2(S*cs - m + bias) as bf16 B-operands, row sums into lsum.
-  // mode 0: plain; 1: diagonal block (causal mask); 2: pseudo-keys (slots >=
-  // nvalid masked).  Key-in-chunk of accumulator register r: 8*(r/4) + 4*hh + r%4.
-  auto softmax = [&](const f32x16& S, int nt, int kc, int mode, int nvalid, float bias, bf16x8 (&pk)[2])
-      __attribute__((always_inline)) {
-    const float mb = mref[nt] - bias;
-    const float sc = F8 ? cs[nt] : a.scale_log2;
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-      float x = __builtin_fmaf(S[r], sc, -mb);
-      if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
-      if (mode == 2 && kic >= nvalid) x = -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(x);
-      sum += p;
-      pk[r >> 3][r & 7] = (__bf16)p;
-    }
-    lsum[nt] += sum;
-  };
-  auto pv = [&](const bf16x8 (&vop)[C::MT][2], const bf16x8 (&pk)[2], int nt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-        O[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mt][ks2], pk[ks2], O[mt][nt], 0, 0, 0);
-  };
-
-  // Interleave hint for one pipeline stage: nmfma MFMAs, each followed by a
-  // slice of the stage's VALU work (the softmax of the other column set).
-  auto interleave = [&](int nmfma, auto nvalu) __attribute__((always_inline)) {
-    for (int k = 0; k < nmfma; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);  // VALU
-    }
-  };
-  using V5 = std::integral_constant<int, 5>;
-  using V16 = std::integral_constant<int, 16>;
-
-  // The NCH 32-key chunks of one bf16 K/V tile (or of one pseudo-key tile),
-  // software-pipelined in two stages per chunk c:
-  //   stage 1: softmax(S_c, columns 0)  ||  QK(c+1, columns 0), PV(c-1, columns 1)
-  //   stage 2: softmax(S_c, columns 1)  ||  QK(c+1, columns 1), PV(c, columns 0)
-  // so the exp/sum/convert VALU work of one column set runs under the MFMAs of
-  // the other; PV(last, columns 1) closes the tile.  Operand buffers are
-  // indexed by chunk parity (no register copies after unrolling), and the
-  // tile base offsets go through readfirstlane so every LDS operand address
-  // is one base register plus a 16-bit immediate.
-  auto run_tile = [&](const char* kt, const char* vt, int nch, int mode, int nvalid, float bias,
-                      const bf16x8 (&qq)[NT][C::KS], int dq) __attribute__((always_inline)) {
-    const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
-    const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
-    const char* kbase = lds + kbo;
-    const char* vbase = lds + vbo;
-    bf16x8 kop[C::KS];
-    bf16x8 vop[2][C::MT][2];
-    bf16x8 p0[2], p1[2][2];
-    f32x16 S[2][2];
-    load_kop(kbase, 0, kop);
-    load_vop(vbase, 0, vop[0]);
-    S[0][0] = qk(kop, qq[0]);
-    S[0][1] = qk(kop, qq[1]);
-#pragma unroll
-    for (int c = 0; c < C::KC; ++c) {
-      if (c >= nch) break;
-      const int cp = c & 1, np = cp ^ 1;
-      const bool more = c + 1 < nch;
-      if (more) load_kop(kbase, c + 1, kop);
-      dma_some(dq);
-      // stage 1
-      softmax(S[cp][0], 0, c, mode, nvalid, bias, p0);
-      if (more) S[np][0] = qk(kop, qq[0]);
-      if (c > 0) pv(vop[np], p1[np], 1);
-      interleave(c > 0 ? 2 * C::KS : C::KS, V5{});
-      __builtin_amdgcn_sched_barrier(0);
-      // stage 2
-      if (more) load_vop(vbase, c + 1, vop[np]);
-      softmax(S[cp][1], 1, c, mode, nvalid, bias, p1[cp]);
-      if (more) S[np][1] = qk(kop, qq[1]);
-      pv(vop[cp], p0, 0);
-      interleave(C::KS + 2 * C::MT, V5{});
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const int lp = (nch - 1) & 1;
-    pv(vop[lp], p1[lp], 1);
-  };
-
-  // ===================== fp8 operand path (32x32x64 MFMA) ==================
-  //  K (A side of S^T): lane (x, hh) reads 32 bytes of key row x at d =
-  //  64ks + 32hh, matching the Q operand.
-  //  P^T (B side of O^T): for a 64-key superchunk, bytes 0..15 of lane (n,
-  //  hh) are the accumulator registers of its first 32-key chunk, bytes
-  //  16..31 those of the second, i.e. byte e is key 32(e/16) + 8((e%16)/4) +
-  //  4hh + e%4.  The MFMA's k-block 0 (bytes 0..15 of both lane halves) is
-  //  thus exactly the first chunk and k-block 1 the second, and the E8M0
-  //  scale of k-block kb of column n is read from lane n + 32kb: P is stored
-  //  per (query, chunk) as P' = P * 2^-b with b chosen from the chunk's max,
-  //  so that P' lies in [128, 256) at the max, and 2^b is applied inside the
-  //  MFMA (no fp8 overflow, full e4m3 precision for the largest terms).
-  //  V^T (A side of O^T): ds_read_b64_tr_b8 returns to lane i of a 16-lane
-  //  group byte e = byte i%8 of the row addressed by source lane 2e + i/8, so
-  //  source lanes 2e, 2e+1 address the same key (the P byte order above) at d
-  //  and d + 8; four reads (+16 keys each) fill the 32 bytes.
-  const int koff8 = l32 * C::RS + 32 * hh;
-  const int L16 = lane & 15;
-  const int voff8 = (8 * (L16 >> 3) + 4 * hh + ((L16 >> 1) & 3)) * C::RS + 16 * ((lane >> 4) & 1) + 8 * (L16 & 1);
-  auto load_kop8 = [&](const char* kt, int kc, i32x8 (&kop)[C::KS8]) __attribute__((always_inline)) {
-    const char* kb = kt + kc * 32 * C::RS + koff8;
-#pragma unroll
-    for (int ks = 0; ks < C::KS8; ++ks) {
-      const i32x4 lo = *(const i32x4*)(kb + 64 * ks);
-      const i32x4 hi = *(const i32x4*)(kb + 64 * ks + 16);
-      kop[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
-  auto load_vop8 = [&](const char* vt, int sc, i32x8 (&vop)[C::MT]) __attribute__((always_inline)) {
-    const char* vb = vt + sc * 64 * C::RS + voff8;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      i32x2 r[4];
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-        r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2*)(vb + 32 * mt + 16 * t4 * C::RS));
-      vop[mt] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-    }
-  };
-  auto qk8 = [&](const i32x8 (&kop)[C::KS8], int nt) __attribute__((always_inline)) -> f32x16 {
-    f32x16 S = f32x16{};
-    if constexpr (F8) {
-#pragma unroll
-      for (int ks = 0; ks < C::KS8; ++ks)
-        S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[ks], qop[nt][ks], S, 0, 0, 0, 0, 0, 0);
-    }
-    return S;
-  };
-  // Superchunk softmax of column set nt: Sn[q] is the S^T chunk 2sc + q.
-  // mode 1 applies the causal mask (diagonal block).
-  auto softmax8 = [&](f32x16 (&Sn)[2], int nt, int sc, int mode, i32x8& pk, int& sbyte)
-      __attribute__((always_inline)) {
-    float bias[2];
-    int bq[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (mode == 1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-          if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
-        }
-      }
-      float m = fmaxf(Sn[q][0], Sn[q][1]);
-#pragma unroll
-      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(Sn[q][r], Sn[q][r + 1]));
-      m = fmaxf(m, partner32(m));
-      float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
-      fx = fminf(fmaxf(fx, -110.f), 120.f);
-      bq[q] = (int)fx - 7;
-      bias[q] = mref[nt] + (float)bq[q];
-    }
-    sbyte = 127 + (hh ? bq[1] : bq[0]);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias[q]));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias[q]));
-        const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias[q]));
-        const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias[q]));
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-        pk[4 * q + j] = w;
-      }
-    }
-  };
-  const i32x8 ones8 = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                            0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
-  auto pv8 = [&](const i32x8 (&vop)[C::MT], const i32x8& pk, int sbyte, int nt) __attribute__((always_inline)) {
-    if constexpr (F8) {
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
-        O[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mt], pk, O[mt][nt], 0, 0, 0, 127, 0, sbyte);
-      Lacc[nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pk, Lacc[nt], 0, 0, 0, 127, 0, sbyte);
-    }
-  };
-  // The NSC superchunks of one fp8 K/V tile, pipelined like run_tile with
-  // 64-key steps:
-  //   stage A: softmax(S_sc, columns 0) || QK(sc+1, columns 0), PV(sc-1, columns 1)
-  //   stage B: softmax(S_sc, columns 1) || QK(sc+1, columns 1), PV(sc, columns 0)
-  auto run_tile8 = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
-    const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
-    const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
-    const char* kbase = lds + kbo;
-    const char* vbase = lds + vbo;
-    i32x8 kop[2][C::KS8];
-    i32x8 vop[2][C::MT];
-    i32x8 pp0, pp1[2];
-    int sb0, sb1[2];
-    f32x16 S[2][NT][2];
-    load_kop8(kbase, 0, kop[0]);
-    load_kop8(kbase, 1, kop[1]);
-    load_vop8(vbase, 0, vop[0]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      S[0][nt][0] = qk8(kop[0], nt);
-      S[0][nt][1] = qk8(kop[1], nt);
-    }
-#pragma unroll
-    for (int sc = 0; sc < C::NSC; ++sc) {
-      const int cp = sc & 1, np = cp ^ 1;
-      const bool more = sc + 1 < C::NSC;
-      if (more) {
-        load_kop8(kbase, 2 * sc + 2, kop[0]);
-        load_kop8(kbase, 2 * sc + 3, kop[1]);
-      }
-      dma_some(dq);
-      // stage A
-      softmax8(S[cp][0], 0, sc, mode, pp0, sb0);
-      if (more) {
-        S[np][0][0] = qk8(kop[0], 0);
-        S[np][0][1] = qk8(kop[1], 0);
-      }
-      if (sc > 0) pv8(vop[np], pp1[np], sb1[np], 1);
-      interleave((more ? 2 * C::KS8 : 0) + (sc > 0 ? C::MT + 1 : 0), V16{});
-      __builtin_amdgcn_sched_barrier(0);
-      // stage B
-      if (more) load_vop8(vbase, sc + 1, vop[np]);
-      softmax8(S[cp][1], 1, sc, mode, pp1[cp], sb1[cp]);
-      if (more) {
-        S[np][1][0] = qk8(kop[0], 1);
-        S[np][1][1] = qk8(kop[1], 1);
-      }
-      pv8(vop[cp], pp0, sb0, 0);
-      interleave((more ? 2 * C::KS8 : 0) + C::MT + 1, V16{});
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    constexpr int lp = (C::NSC - 1) & 1;
-    pv8(vop[lp], pp1[lp], sb1[lp], 1);
-  };
-
-  // dq: next-block copy ops to issue per chunk (per superchunk in fp8)
-  auto run_main = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
-    if constexpr (F8) {
-      run_tile8(kt, vt, mode, dq);
-    } else {
-      run_tile(kt, vt, C::KC, mode, 0, 0.f, qop, dq);
-    }
-  };
-
-
-  // ---- kept blocks (sparse) or all blocks j <= i (dense)
-  const long mrow = ((long)s * a.Hkv + h) * a.seq.nqb_stride + il;
-  const int* list = a.sparse ? a.block_idx + mrow * a.seq.nkb_stride : nullptr;
-  const int nblk = a.sparse ? a.block_cnt[mrow] : i + 1;
-  const int j0 = a.sparse ? list[0] : 0;
-
-  // Reference max per query row: max logit over the first 32 keys of the
-  // first block (causally masked if that block is the diagonal), + margin.
-  issue_load(j0, 0, load_pids(j0));
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  {
-    f32x16 S0[NT];
-    if constexpr (F8) {
-      i32x8 kop[C::KS8];
-      load_kop8(lds, 0, kop);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S0[nt] = qk8(kop, nt);
-    } else {
-      bf16x8 kop[C::KS];
-      load_kop(lds, 0, kop);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S0[nt] = qk_chain(kop, qop[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-        float x = S0[nt][r] * cs[nt];
-        if (j0 == i && kic > rib[nt]) x = -INFINITY;
-        m = fmaxf(m, x);
-      }
-      m = fmaxf(m, partner32(m));
-      mref[nt] = (m > -INFINITY ? m : 0.f) + kRefMargin;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-#pragma unroll 1
-  for (int pass = 0; pass < kMaxPasses; ++pass) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) O[mt][nt] = f32x16{};
-      lsum[nt] = 0.f;
-      if constexpr (F8) Lacc[nt] = f32x16{};
-    }
-    if (pass > 0) {
-      __syncthreads();
-      issue_load(j0, 0, load_pids(j0));
-    }
-    // Blocks 0 .. nblk-2 are strictly below the diagonal (the list is
-    // ascending and ends with block i): one unmasked loop, the diagonal block
-    // peeled after it.  List entries are read two blocks ahead so that the
-    // address of the next K/V prefetch never waits on memory.
-    // Paged: the page ids of the block after next are loaded together with
-    // the copies of the next block.
-    int jnext = nblk > 1 ? (a.sparse ? list[1] : 1) : 0;
-    int jafter = nblk > 2 ? (a.sparse ? list[2] : 2) : 0;
-    int pnext = load_pids(jnext);
-    for (int n = 0; n + 1 < nblk; ++n) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      const int jafter2 = n + 3 < nblk ? (a.sparse ? list[n + 3] : n + 3) : 0;
-      const int pafter = load_pids(jafter);
-      issue_load(jnext, (n + 1) & 1, pnext);
-      const char* kt = lds + (n & 1) * C::TILE;
-      const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      run_main(kt, vt, 0, 0);
-      jnext = jafter;
-      jafter = jafter2;
-      pnext = pafter;
-    }
-    {
-      const int n = nblk - 1;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      const char* kt = lds + (n & 1) * C::TILE;
-      const char* vt = lds + (2 + (n & 1)) * C::TILE;
-      run_main(kt, vt, 1, 0);
-    }
-
-    // ---- mean correction: dropped blocks as pseudo-keys
-    // LDS during this phase: pseudo-K tile (32 rows, bf16) | pseudo-V tile |
-    // ndrop | kept-block bitmap | dropped-block list | 2 staging buffers of
-    // the fp32 kbar/vbar rows of a 32-pseudo-key chunk (global_load_lds,
-    // one chunk ahead of the compute).  In fp8 the pseudo rows are divided
-    // by the head's k / v scale so that they share the code units of the
-    // fp8 K and V (the logit scale cs and the output scale v_s then apply
-    // to both), and Q is widened to bf16 (exact for e4m3 values).
-    if (a.sparse && a.mean_correction && i > 0) {
-      __syncthreads();
-      char* pk_t = lds;
-      char* pv_t = lds + C::PSB;
-      int* ndrop_slot = (int*)(lds + 2 * C::PSB);
-      uint32_t* bm = (uint32_t*)(ndrop_slot + 1);
-      const int nwords = (i + 31) >> 5;
-      int* drop = (int*)(bm + nwords);
-      char* stage = lds + corr_stage_offset<D, BLK, F8>(a.seq.nkb_stride);
-      for (int w = tid; w < nwords; w += nthr) bm[w] = 0u;
-      __syncthreads();
-      for (int n = tid; n < nblk; n += nthr) {
-        const int j = list[n];
-        if (j < i) atomicOr(&bm[j >> 5], 1u << (j & 31));
-      }
-      __syncthreads();
-      if (wave == 0) {
-        int total = 0;
-        for (int w0 = 0; w0 < nwords; w0 += 64) {
-          const int w = w0 + lane;
-          uint32_t bits = 0u;
-          if (w < nwords) {
-            const uint32_t valid = (w < (i >> 5)) ? 0xffffffffu : ((1u << (i & 31)) - 1u);
-            bits = ~bm[w] & valid;
-          }
-          const int cnt = __popc(bits);
-          const int incl = wave_incl_scan(cnt);
-          int off = total + incl - cnt;
-          while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1u;
-            drop[off++] = w * 32 + b;
-          }
-          total += __shfl(incl, 63, 64);
-        }
-        if (lane == 0) *ndrop_slot = total;
-      }
-      __syncthreads();
-      const int ndrop = *ndrop_slot;
-      const float* kbr = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
-      const float* vbr = a.vbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
-      const float bias = log2f((float)BLK);  // ln(n_j) in log2 units; dropped blocks are full
-      const float kmul = F8 ? 1.f / a.k_scale[h] : 1.f;
-      const float vmul = F8 ? 1.f / a.v_scale[h] : 1.f;
-      bf16x8 q16[NT][C::KS];
-      if constexpr (F8) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) {
-            const i32x8 w = qop[nt][ks >> 2];
-            const uint32_t w0 = (uint32_t)w[2 * (ks & 3)], w1 = (uint32_t)w[2 * (ks & 3) + 1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              q16[nt][ks][e] = (__bf16)fp8_byte_to_f32(w0, e);
-              q16[nt][ks][4 + e] = (__bf16)fp8_byte_to_f32(w1, e);
-            }
-          }
-      }
-      // stage chunk c (32 rows of kbar then 32 rows of vbar, fp32) into buffer bb
-      auto stage_load = [&](int c0, int bb) __attribute__((always_inline)) {
-        constexpr int LPR = D * 4 / 16;        // lanes per fp32 row
-        constexpr int RPO = 64 / LPR;          // rows per wave op
-        for (int it = wave; it < 64 / RPO; it += nwaves) {
-          const int rr = it * RPO + lane / LPR;   // 0..63: K rows then V rows
-          const int r32 = rr & 31;
-          const int id = c0 + r32 < ndrop ? drop[c0 + r32] : 0;
-          const float* src = (rr < 32 ? kbr : vbr) + (long)id * D + (lane % LPR) * 4;
-          __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + bb * C::STG + it * 1024), 16, 0,
-                                           0);
-        }
-      };
-      constexpr int CH8 = D / 8;  // 8-element pieces per row
-      if (ndrop > 0) stage_load(0, 0);
-      for (int c0 = 0, cc = 0; c0 < ndrop; c0 += 32, ++cc) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (c0 + 32 < ndrop) stage_load(c0 + 32, (cc + 1) & 1);
-        const char* sb = stage + (cc & 1) * C::STG;
-        for (int task = tid; task < 2 * 32 * CH8; task += nthr) {
-          const int rr = task / CH8;            // 0..63
-          const int c = task - rr * CH8;
-          const float f = rr < 32 ? kmul : vmul;
-          const float4 x0 = *(const float4*)(sb + rr * D * 4 + c * 32);
-          const float4 x1 = *(const float4*)(sb + rr * D * 4 + c * 32 + 16);
-          const uint4 w = make_uint4(pack_bf16x2(x0.x * f, x0.y * f), pack_bf16x2(x0.z * f, x0.w * f),
-                                     pack_bf16x2(x1.x * f, x1.y * f), pack_bf16x2(x1.z * f, x1.w * f));
-          *(uint4*)((rr < 32 ? pk_t : pv_t) + (rr & 31) * C::RS16 + c * 16) = w;
-        }
-        __syncthreads();
-        if constexpr (F8) {
-          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, q16, 0);
-        } else {
-          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, qop, 0);
-        }
-      }
-    }
-
-    // A row whose normaliser overflowed the range reruns the tile with its
-    // reference moved up (all rows of the workgroup take part in the rerun;
-    // rows that were fine recompute the same values).
-    bool bad = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float lt = (F8 ? Lacc[nt][0] : 0.f) + lsum[nt] + partner32(lsum[nt]);
-      if (!(lt < __builtin_exp2f(kRefOverflow))) {
-        bad = true;
-        mref[nt] += (lt < INFINITY) ? log2f(lt) : kRefOverflow;
-      }
-    }
-    if (!__syncthreads_or(bad)) break;
-  }
-
-  // ---- epilogue: O = O^T / l (fp8: times the head's v scale), LSE
-  const bool out32 = a.out_fp32;
-  const float oscale = F8 ? a.v_scale[h] : 1.f;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    int rb;
-    long off;
-    const bool ok = qinfo(nt, rb, off);
-    const float lt = (F8 ? Lacc[nt][0] : 0.f) + lsum[nt] + partner32(lsum[nt]);
-    const float inv = oscale / lt;
-    if (ok) {
-      if (a.lse && hh == 0) {
-        const int gq = (pr0 + l32 + 32 * nt) / BLK;
-        const int r = i * BLK + rb - g.P;
-        const long li = a.seq.cu_seqlens_q ? (long)(g.qrow0 + r) * a.Hq + h * G + gq
-                                           : ((long)s * a.Hq + h * G + gq) * a.lse_stride + r;
-        a.lse[li] = (mref[nt] + log2f(lt)) * kLn2;
-      }
-      if (out32) {
-        float* dst = (float*)a.out + off + 4 * hh;
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *(float4*)(dst + 32 * mt + 8 * q4) =
-                make_float4(O[mt][nt][4 * q4] * inv, O[mt][nt][4 * q4 + 1] * inv, O[mt][nt][4 * q4 + 2] * inv,
-                            O[mt][nt][4 * q4 + 3] * inv);
-      } else {
-        __bf16* dst = (__bf16*)a.out + off + 4 * hh;
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *(uint2*)(dst + 32 * mt + 8 * q4) =
-                make_uint2(pack_bf16x2(O[mt][nt][4 * q4] * inv, O[mt][nt][4 * q4 + 1] * inv),
-                           pack_bf16x2(O[mt][nt][4 * q4 + 2] * inv, O[mt][nt][4 * q4 + 3] * inv));
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Persistent tile scheduler.  The tiles t = 0 .. ntiles-1 (longest first)
-// form 8 queues, queue q = {t : t % 8 == q}, one per XCD under the
-// round-robin workgroup -> XCD dispatch; the gridDim.x <= #CU workgroups stay
-// resident, workgroup w starts with tile w of its home queue w % 8 and then
-// pulls the next position of its queue from a device-scope counter, moving
-// on to the other queues in turn once its own is drained.  Workgroups never
-// wait for the hardware dispatcher between tiles (with tiles of very
-// different lengths that dispatcher leaves CUs idle), while the two parts of
-// one tile and the tiles of one head in a query-block rank stay in one XCD's
-// L2.  g_sched holds one set of 8 counters (each on its own 128-byte line)
-// per launch slot; the launcher zeroes the slot's counters with
-// sched_reset_kernel on the same stream right before the launch, and hands
-// out slots round-robin so that launches running concurrently on different
-// streams use different counters.
-constexpr int kSchedSlots = 64;
-__device__ unsigned int g_sched[kSchedSlots][8][32];
-
-__global__ void sched_reset_kernel(int slot) {
-  if (threadIdx.x < 8) atomicExch(&g_sched[slot][threadIdx.x][0], 0u);
-}
-
-template <int D, int BLK, bool F8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_kernel(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int nwg = gridDim.x;
-  const int home = blockIdx.x & 7;
-  unsigned int(*ctr)[32] = g_sched[a.sched_slot];
-  // next-tile broadcast, double-buffered: the slot written at iteration k is
-  // rewritten at k+2, after every thread has passed the barrier of k+1
-  volatile int* next_slot = (volatile int*)(smem + a.lds_sched);
-  int tile = blockIdx.x;
-  int qi = 0;        // thread 0: queues drained so far
-  unsigned pre = 0;  // thread 0: position fetched from queue (home + qi) % 8
-  for (int k = 0;; ++k) {
-    if (threadIdx.x == 0 && qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
-    attn_tile<D, BLK, F8>(a, tile, smem);
-    if (threadIdx.x == 0) {
-      int nxt = -1;
-      while (qi < 8) {
-        const int q = (home + qi) & 7;
-        const int pos = (nwg - q + 7) / 8 + (int)pre;  // the home workgroups took positions [0, nhome)
-        if (8 * pos + q < a.ntiles) {
-          nxt = 8 * pos + q;
-          break;
-        }
-        if (++qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
-      }
-      next_slot[k & 1] = nxt;
-    }
-    __syncthreads();
-    tile = __builtin_amdgcn_readfirstlane(next_slot[k & 1]);
-    if (tile < 0) break;
-  }
-}
-
-// LDS bytes the attention kernel needs for a given key-block count.
-template <int D, int BLK, bool F8>
-static size_t attn_lds_bytes(int nkb) {
-  using C = Cfg<D, BLK, F8>;
-  size_t lds = 4 * (size_t)C::TILE;
-  const size_t corr = (size_t)corr_stage_offset<D, BLK, F8>(nkb) + 2 * (size_t)C::STG;
-  return corr > lds ? corr : lds;
-}
-
-static int compute_units() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  if (dev >= 64) dev = 63;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
-static std::atomic<unsigned> g_slot_counter{0};
-
-template <int D, int BLK, bool F8>
-static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
-  const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
-  const size_t lds = attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
-  const size_t lds_total = lds + 16;  // + the next-tile broadcast slots
-  if (lds_total > 160 * 1024) return hipErrorInvalidValue;
-  if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_total);
-  if (e != hipSuccess) return e;
-  if (ntiles == 0) return hipSuccess;
-  AttnArgs a = a0;
-  a.ntiles = (int)ntiles;
-  a.sched_slot = (int)(g_slot_counter.fetch_add(1) % kSchedSlots);
-  a.lds_sched = (int)lds;
-  const long grid = ntiles < compute_units() ? ntiles : compute_units();
-  hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, st, a.sched_slot);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_kernel<D, BLK, F8>), dim3((unsigned)grid), dim3(64 * a.waves), lds_total, st, a);
-  return hipGetLastError();
-}
-
 size_t attention_lds_bytes(int D, int block, int nkb, int fp8) {
-  if (fp8) {
-    if (D == 128 && block == 128) return attn_lds_bytes<128, 128, true>(nkb);
-    if (D == 128 && block == 64) return attn_lds_bytes<128, 64, true>(nkb);
-    if (D == 64 && block == 128) return attn_lds_bytes<64, 128, true>(nkb);
-    if (D == 64 && block == 64) return attn_lds_bytes<64, 64, true>(nkb);
-    return 0;
-  }
-  if (D == 128 && block == 128) return attn_lds_bytes<128, 128, false>(nkb);
-  if (D == 128 && block == 64) return attn_lds_bytes<128, 64, false>(nkb);
-  if (D == 64 && block == 128) return attn_lds_bytes<64, 128, false>(nkb);
-  if (D == 64 && block == 64) return attn_lds_bytes<64, 64, false>(nkb);
-  return 0;
+  return fp8 ? attention_lds_bytes_fp8(D, block, nkb) : attention_lds_bytes_bf16(D, block, nkb);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t st) {
-  if (fp8) {
-    if (D == 128 && block == 128) return launch_t<128, 128, true>(a, st);
-    if (D == 128 && block == 64) return launch_t<128, 64, true>(a, st);
-    if (D == 64 && block == 128) return launch_t<64, 128, true>(a, st);
-    if (D == 64 && block == 64) return launch_t<64, 64, true>(a, st);
-    return hipErrorNotSupported;
-  }
-  if (D == 128 && block == 128) return launch_t<128, 128, false>(a, st);
-  if (D == 128 && block == 64) return launch_t<128, 64, false>(a, st);
-  if (D == 64 && block == 128) return launch_t<64, 128, false>(a, st);
-  if (D == 64 && block == 64) return launch_t<64, 64, false>(a, st);
-  return hipErrorNotSupported;
+  return fp8 ? launch_attention_fp8(a, D, block, st) : launch_attention_bf16(a, D, block, st);
 }
 
 }  // namespace fp2

@@ -87,5 +87,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t s);
 // Dynamic LDS bytes of the attention kernel (0 for an unsupported shape).
 size_t attention_lds_bytes(int D, int block, int nkb, int fp8);
+hipError_t launch_attention_bf16(const AttnArgs& a, int D, int block, hipStream_t s);
+hipError_t launch_attention_fp8(const AttnArgs& a, int D, int block, hipStream_t s);
+size_t attention_lds_bytes_bf16(int D, int block, int nkb);
+size_t attention_lds_bytes_fp8(int D, int block, int nkb);
 
 }  // namespace fp2
