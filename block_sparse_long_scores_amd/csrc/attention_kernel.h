@@ -499,10 +499,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
           if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
         }
       }
-      float m = fmaxf(Sn[q][0], Sn[q][1]);
+      // NaN-propagating maximum (v_maximum3_f32): no canonicalizing copies of
+      // the MFMA results, which fmaxf needs in IEEE mode
+      float m = __builtin_elementwise_maximum(Sn[q][0], Sn[q][1]);
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(Sn[q][r], Sn[q][r + 1]));
-      m = fmaxf(m, partner32(m));
+      for (int r = 2; r < 16; r += 2)
+        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(Sn[q][r], Sn[q][r + 1]));
+      m = __builtin_elementwise_maximum(m, partner32(m));
       float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
       fx = fminf(fmaxf(fx, -110.f), 120.f);
       bq[q] = (int)fx - 7;
@@ -533,10 +536,12 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
       Lacc[nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pk, Lacc[nt], 0, 0, 0, 127, 0, sbyte);
     }
   };
-  // The NSC superchunks of one fp8 K/V tile, pipelined like run_tile with
-  // 64-key steps:
-  //   stage A: softmax(S_sc, columns 0) || QK(sc+1, columns 0), PV(sc-1, columns 1)
-  //   stage B: softmax(S_sc, columns 1) || QK(sc+1, columns 1), PV(sc, columns 0)
+  // The NSC superchunks of one fp8 K/V tile, two stages per superchunk sc:
+  //   stage X: softmax(S_sc, columns 0) || QK(sc, columns 1), PV(sc-1, columns 1)
+  //   stage Y: softmax(S_sc, columns 1) || PV(sc, columns 0), QK(sc+1, columns 0)
+  // so that only two S sets (one per column set) are ever live.  The K
+  // operands of superchunk sc+1 are read at the start of stage Y, behind the
+  // PV MFMAs; the V operands are double-buffered by superchunk parity.
   auto run_tile8 = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
     const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
     const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
@@ -544,48 +549,41 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
     const char* vbase = lds + vbo;
     i32x8 kop[2][C::KS8];
     i32x8 vop[2][C::MT];
-    i32x8 pp0, pp1[2];
-    int sb0, sb1[2];
-    f32x16 S[2][NT][2];
+    i32x8 pp0, pp1;
+    int sb0 = 0, sb1 = 0;
+    f32x16 S0[2], S1[2];
     load_kop8(kbase, 0, kop[0]);
     load_kop8(kbase, 1, kop[1]);
-    load_vop8(vbase, 0, vop[0]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      S[0][nt][0] = qk8(kop[0], nt);
-      S[0][nt][1] = qk8(kop[1], nt);
-    }
+    S0[0] = qk8(kop[0], 0);
+    S0[1] = qk8(kop[1], 0);
 #pragma unroll
     for (int sc = 0; sc < C::NSC; ++sc) {
-      const int cp = sc & 1, np = cp ^ 1;
+      const int cp = sc & 1;
       const bool more = sc + 1 < C::NSC;
+      // stage X
+      load_vop8(vbase, sc, vop[cp]);
+      dma_some(dq);
+      softmax8(S0, 0, sc, mode, pp0, sb0);
+      S1[0] = qk8(kop[0], 1);
+      S1[1] = qk8(kop[1], 1);
+      if (sc > 0) pv8(vop[cp ^ 1], pp1, sb1, 1);
+      interleave(2 * C::KS8 + (sc > 0 ? C::MT + 1 : 0), V16{});
+      __builtin_amdgcn_sched_barrier(0);
+      // stage Y
       if (more) {
         load_kop8(kbase, 2 * sc + 2, kop[0]);
         load_kop8(kbase, 2 * sc + 3, kop[1]);
       }
-      dma_some(dq);
-      // stage A
-      softmax8(S[cp][0], 0, sc, mode, pp0, sb0);
-      if (more) {
-        S[np][0][0] = qk8(kop[0], 0);
-        S[np][0][1] = qk8(kop[1], 0);
-      }
-      if (sc > 0) pv8(vop[np], pp1[np], sb1[np], 1);
-      interleave((more ? 2 * C::KS8 : 0) + (sc > 0 ? C::MT + 1 : 0), V16{});
-      __builtin_amdgcn_sched_barrier(0);
-      // stage B
-      if (more) load_vop8(vbase, sc + 1, vop[np]);
-      softmax8(S[cp][1], 1, sc, mode, pp1[cp], sb1[cp]);
-      if (more) {
-        S[np][1][0] = qk8(kop[0], 1);
-        S[np][1][1] = qk8(kop[1], 1);
-      }
+      softmax8(S1, 1, sc, mode, pp1, sb1);
       pv8(vop[cp], pp0, sb0, 0);
-      interleave((more ? 2 * C::KS8 : 0) + C::MT + 1, V16{});
+      if (more) {
+        S0[0] = qk8(kop[0], 0);
+        S0[1] = qk8(kop[1], 0);
+      }
+      interleave(C::MT + 1 + (more ? 2 * C::KS8 : 0), V16{});
       __builtin_amdgcn_sched_barrier(0);
     }
-    constexpr int lp = (C::NSC - 1) & 1;
-    pv8(vop[lp], pp1[lp], sb1[lp], 1);
+    pv8(vop[(C::NSC - 1) & 1], pp1, sb1, 1);
   };
 
   // dq: next-block copy ops to issue per chunk (per superchunk in fp8)
