@@ -87,6 +87,19 @@ __host__ __device__ constexpr int corr_stage_offset(int nkb) {
   return ((2 * Cfg<D, BLK, F8>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb + 1023) / 1024) * 1024;
 }
 
+// LDS transpose reads.  The K/V tiles a block reads were completed by an
+// explicit s_waitcnt + barrier at the start of that block, while the copies
+// in flight during it fill the other buffer.  The restrict-qualified pointer
+// gives the read alias-scope information after inlining, which keeps the
+// compiler from waiting on those in-flight LDS-DMA copies before each read
+// (plain LDS loads carry type-based alias information and are not held).
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)p);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = __lane_id();
 #pragma unroll
@@ -334,10 +347,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
     for (int mt = 0; mt < C::MT; ++mt) {
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + 16 * ks2 * C::RS16));
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + 64 * mt + (16 * ks2 + 8) * C::RS16));
+        const i16x4 v0 = lds_read_tr16(vb + 64 * mt + 16 * ks2 * C::RS16);
+        const i16x4 v1 = lds_read_tr16(vb + 64 * mt + (16 * ks2 + 8) * C::RS16);
         vop[mt][ks2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
@@ -470,8 +481,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
       i32x2 r[4];
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
-        r[t4] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2*)(vb + 32 * mt + 16 * t4 * C::RS));
+        r[t4] = lds_read_tr8(vb + 32 * mt + 16 * t4 * C::RS);
       vop[mt] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
     }
   };
@@ -651,7 +661,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
     }
     // Blocks 0 .. nblk-2 are strictly below the diagonal (the list is
     // ascending and ends with block i): one unmasked loop, the diagonal block
-    // peeled after it.  List entries are read two blocks ahead so that the
+    // peeled after it.  List entries are read three blocks ahead so that the
     // address of the next K/V prefetch never waits on memory.
     // Paged: the page ids of the block after next are loaded together with
     // the copies of the next block.
