@@ -262,7 +262,7 @@ void fp2_paged_mask_dims(const fp2_params* p, int32_t max_seqlen_q, int32_t max_
 
 namespace {
 struct PagedLayout {
-  size_t qbar, kbar, vbar, idx, cnt, total;
+  size_t qbar, kbar, vbar, idx, cnt, plan, total;
 };
 PagedLayout paged_layout(const fp2_params* p, int n, int max_nqb, int max_nkb) {
   PagedLayout L{};
@@ -278,6 +278,8 @@ PagedLayout paged_layout(const fp2_params* p, int n, int max_nqb, int max_nkb) {
   off += align_up((size_t)n * H * max_nqb * max_nkb * 4);
   L.cnt = off;
   off += align_up((size_t)n * H * max_nqb * 4);
+  L.plan = off;  // task count, then the work-ordered task list
+  off += align_up(16 + (size_t)n * H * max_nqb * 4);
   L.total = off;
   return L;
 }
@@ -384,8 +386,20 @@ fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const
   sa.rows_per_wg = tq;
   e = launch_select(sa, s);
   if (e != hipSuccess) return device_status(e, "select kernel launch");
+  PlanArgs pl{};
+  pl.seq = sd;
+  pl.block_cnt = cnt;
+  pl.plan_count = (int32_t*)(ws + L.plan);
+  pl.plan = (int32_t*)(ws + L.plan + 16);
+  pl.Hkv = p->num_kv_heads;
+  pl.block = b;
+  pl.mean_correction = p->mean_correction;
+  e = launch_plan(pl, s);
+  if (e != hipSuccess) return device_status(e, "plan kernel launch");
   AttnArgs a{};
   fill_attn_common(a, p);
+  a.plan = pl.plan;
+  a.plan_count = pl.plan_count;
   a.seq = sd;
   a.kv = kv;
   a.q = q;

@@ -154,7 +154,7 @@ __device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[4], const bf16x8 (&
 // the 256-row part `part` of them, over its kept key blocks (or all blocks
 // j <= i when dense), then the mean correction and the epilogue.
 template <int D, int BLK, bool F8>
-__device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, char* smem) {
+__device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const int pos, char* smem) {
   using C = Cfg<D, BLK, F8>;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -164,19 +164,35 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
   const int hh = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- tile.  Query blocks go from the last (longest) down; the G2 =
-  // Hkv*batch*parts tiles of one query block are rotated by the query-block
-  // rank, so that the XCD queue tile % 8 serves every head in turn (kept-block
-  // counts differ between heads) while the parts of one tile share a queue.
-  const int G2 = a.Hkv * a.seq.batch * a.parts;
-  const int rank = tile / G2;
-  int t = (tile - rank * G2 + rank) % G2;
-  const int h = t % a.Hkv;
-  t /= a.Hkv;
-  const int s = t % a.seq.batch;
-  t /= a.seq.batch;
-  const int part = t;
-  const int il = a.nqb_grid - 1 - rank;
+  // ---- tile (q, pos): position pos of queue q (see attn_kernel).
+  //  Without a plan, tile t = 8*pos + q: query blocks go from the last
+  //  (longest) down; the G2 = Hkv*batch*parts tiles of one query block are
+  //  rotated by the query-block rank, so that queue t % 8 serves every head
+  //  in turn (kept-block counts differ between heads) while the parts of one
+  //  tile share a queue.
+  //  With a plan: task k = 8*(pos / parts) + q of the work-ordered list,
+  //  part pos % parts.
+  int h, s, part, il;
+  if (a.plan) {
+    part = pos % a.parts;
+    const int task = a.plan[8 * (pos / a.parts) + q];
+    const int per_seq = a.Hkv * a.seq.nqb_stride;
+    s = task / per_seq;
+    const int r = task - s * per_seq;
+    h = r / a.seq.nqb_stride;
+    il = r - h * a.seq.nqb_stride;
+  } else {
+    const int tile = 8 * pos + q;
+    const int G2 = a.Hkv * a.seq.batch * a.parts;
+    const int rank = tile / G2;
+    int t = (tile - rank * G2 + rank) % G2;
+    h = t % a.Hkv;
+    t /= a.Hkv;
+    s = t % a.seq.batch;
+    t /= a.seq.batch;
+    part = t;
+    il = a.nqb_grid - 1 - rank;
+  }
   const SeqGeo g = seq_geo(a.seq, s, BLK);
   if (il < 0 || il >= g.nqb) return;
   const int i = g.first_qb + il;
@@ -853,20 +869,19 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int tile, cha
   }
 }
 
-// Persistent tile scheduler.  The tiles t = 0 .. ntiles-1 (longest first)
-// form 8 queues, queue q = {t : t % 8 == q}, one per XCD under the
-// round-robin workgroup -> XCD dispatch; the gridDim.x <= #CU workgroups stay
-// resident, workgroup w starts with tile w of its home queue w % 8 and then
-// pulls the next position of its queue from a device-scope counter, moving
-// on to the other queues in turn once its own is drained.  Workgroups never
-// wait for the hardware dispatcher between tiles (with tiles of very
-// different lengths that dispatcher leaves CUs idle), while the two parts of
-// one tile and the tiles of one head in a query-block rank stay in one XCD's
-// L2.  g_sched holds one set of 8 counters (each on its own 128-byte line)
-// per launch slot; the launcher zeroes the slot's counters with
-// sched_reset_kernel on the same stream right before the launch, and hands
-// out slots round-robin so that launches running concurrently on different
-// streams use different counters.
+// Persistent tile scheduler.  The tiles form 8 queues, one per XCD under the
+// round-robin workgroup -> XCD dispatch, each ordered longest first (see
+// attn_tile).  The gridDim.x <= #CU workgroups stay resident; workgroup w
+// starts at position w / 8 of its home queue w % 8 and then pulls the next
+// position of its queue from a device-scope counter, moving on to the other
+// queues in turn once its own is drained.  Workgroups never wait for the
+// hardware dispatcher between tiles (with tiles of very different lengths that
+// dispatcher leaves CUs idle), while the two parts of one tile and the tiles
+// of one head in a query-block rank stay in one XCD's L2.  g_sched holds one
+// set of 8 counters (each on its own 128-byte line) per launch slot; the
+// launcher zeroes the slot's counters with sched_reset_kernel on the same
+// stream right before the launch, and hands out slots round-robin so that
+// launches running concurrently on different streams use different counters.
 constexpr int kSchedSlots = 64;
 __device__ unsigned int g_sched[kSchedSlots][8][32];
 
@@ -881,31 +896,43 @@ void attn_kernel(AttnArgs a) {
   const int nwg = gridDim.x;
   const int home = blockIdx.x & 7;
   unsigned int(*ctr)[32] = g_sched[a.sched_slot];
+  // tiles in queue q: all positions below it are tiles
+  const int ntask = a.plan ? __builtin_amdgcn_readfirstlane(a.plan_count[0]) : a.ntiles;
+  auto queue_len = [&](int q) -> int {
+    if (!a.plan) return (ntask - q + 7) >> 3;
+    return q < ntask ? ((ntask - q + 7) >> 3) * a.parts : 0;
+  };
   // next-tile broadcast, double-buffered: the slot written at iteration k is
   // rewritten at k+2, after every thread has passed the barrier of k+1
   volatile int* next_slot = (volatile int*)(smem + a.lds_sched);
-  int tile = blockIdx.x;
   int qi = 0;        // thread 0: queues drained so far
   unsigned pre = 0;  // thread 0: position fetched from queue (home + qi) % 8
-  for (int k = 0;; ++k) {
-    if (threadIdx.x == 0 && qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
-    attn_tile<D, BLK, F8>(a, tile, smem);
+  // thread 0: the next tile, encoded q | pos << 3, or -1 when every queue is
+  // drained; `pre` holds a fetch from queue (home + qi) % 8 on entry
+  auto next_tile = [&]() -> int {
+    while (qi < 8) {
+      const int q = (home + qi) & 7;
+      const int pos = (nwg - q + 7) / 8 + (int)pre;  // the home workgroups took positions [0, nhome)
+      if (pos < queue_len(q)) return q | (pos << 3);
+      if (++qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
+    }
+    return -1;
+  };
+  int tile = (int)(blockIdx.x >> 3) < queue_len(home) ? home | ((blockIdx.x >> 3) << 3) : -2;
+  if (tile == -2) {  // no tile at the home position: start by fetching
     if (threadIdx.x == 0) {
-      int nxt = -1;
-      while (qi < 8) {
-        const int q = (home + qi) & 7;
-        const int pos = (nwg - q + 7) / 8 + (int)pre;  // the home workgroups took positions [0, nhome)
-        if (8 * pos + q < a.ntiles) {
-          nxt = 8 * pos + q;
-          break;
-        }
-        if (++qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
-      }
-      next_slot[k & 1] = nxt;
+      pre = atomicAdd(&ctr[home][0], 1u);
+      next_slot[1] = next_tile();
     }
     __syncthreads();
+    tile = __builtin_amdgcn_readfirstlane(next_slot[1]);
+  }
+  for (int k = 0; tile >= 0; ++k) {
+    if (threadIdx.x == 0 && qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
+    attn_tile<D, BLK, F8>(a, tile & 7, tile >> 3, smem);
+    if (threadIdx.x == 0) next_slot[k & 1] = next_tile();
+    __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(next_slot[k & 1]);
-    if (tile < 0) break;
   }
 }
 

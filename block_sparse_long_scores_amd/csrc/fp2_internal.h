@@ -54,6 +54,15 @@ struct SelectArgs {
   int rows_per_wg;          // query blocks per workgroup
 };
 
+// Work-ordered task list of a continuous batch (plan.hip).
+struct PlanArgs {
+  SeqDesc seq;
+  const int* block_cnt;     // [B, Hkv, nqb_stride]
+  int* plan;                // out: task ids (s*Hkv + h)*nqb_stride + il, longest first
+  int* plan_count;          // out: number of tasks
+  int Hkv, block, mean_correction;
+};
+
 struct AttnArgs {
   SeqDesc seq;
   KVDesc kv;
@@ -76,6 +85,8 @@ struct AttnArgs {
   int parts;                // workgroups per (seq, head, q-block) tile
   int waves;                // waves per workgroup
   int nqb_grid;             // query-block extent of the tile space
+  const int* plan;          // optional work-ordered task list (PlanArgs) or nullptr
+  const int* plan_count;
   // set by the launcher
   int ntiles;               // Hkv * batch * parts * nqb_grid
   int sched_slot;           // tile-scheduler counter slot of this launch
@@ -84,6 +95,7 @@ struct AttnArgs {
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int D, int block, int fp8, hipStream_t s);
 // Dynamic LDS bytes of the attention kernel (0 for an unsupported shape).
 size_t attention_lds_bytes(int D, int block, int nkb, int fp8);
