@@ -142,8 +142,9 @@ def timed(stream, fns, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     per = [float(np.mean([row[j].elapsed_time(row[j + 1]) for row in ev])) for j in range(len(fns))]
-    total = float(np.mean([row[0].elapsed_time(row[-1]) for row in ev]))
-    return per, total, wall
+    totals = [row[0].elapsed_time(row[-1]) for row in ev]
+    timed.last_median = float(np.median(totals))
+    return per, float(np.mean(totals)), wall
 
 
 class ContigLayer:
@@ -324,6 +325,7 @@ def main():
     p = fp2.make_params(hq, hkv, d, b, tau=tau)
     L = ContigLayer(fp2, q, k, v, p, S, hkv, d, b)
     (sel_ms, att_ms), step_ms, wall_ms = timed(stream, [L.select, L.attend], args.steps, args.warmup)
+    step_median = timed.last_median
     log(f"[bench] select {sel_ms:.3f} ms, attention {att_ms:.3f} ms, step {step_ms:.3f} ms (wall {wall_ms:.3f})")
 
     F = flops(L.cnt.cpu().numpy(), hq, hkv, d, b, S)
@@ -382,6 +384,7 @@ def main():
             "select_ms": round(sel_ms, 3),
             "sparse_attn_ms": round(att_ms, 3),
             "wall_ms_per_step": round(wall_ms, 3),
+            "median_ms_per_step": round(step_median, 3),
             "block_sparsity": round(F["sparsity"], 4),
             "kept_blocks": F["kept"],
             "executed_tflop": round(F["executed"] / 1e12, 3),
@@ -390,6 +393,8 @@ def main():
             "eff_tflops_executed_attn": round(achieved, 1),
             "dense": res_dense,
             "speedup_vs_dense": round(res_dense["ms"] / step_ms, 2) if res_dense else None,
+            # sparse executed-attention rate / dense rate: the per-block efficiency the sparsity keeps
+            "efficiency_ratio": round(achieved / res_dense["tflops"], 3) if res_dense else None,
             "fp8_128k": res_fp8,
             "paged_batch6": res_paged,
             "kernel_source_hash": kernel_source_hash(),
