@@ -76,15 +76,14 @@ struct Cfg {
   static constexpr int TILE = ((BLK * RS + 1023) / 1024) * 1024;  // one K or V tile
   static constexpr int NLD = TILE / 1024;      // global_load_lds wave ops per tile
   static constexpr int RS16 = 2 * D + (D == 128 ? 32 : 16);  // bf16 pseudo-key rows
-  static constexpr int PSB = 32 * RS16;        // one 32-row pseudo-key tile (bf16)
-  static constexpr int STG = 2 * 32 * D * 4;   // fp32 kbar + vbar rows of one pseudo chunk
+  static constexpr int PSB = BLK * RS16;       // one pseudo-key tile of BLK rows (bf16)
 };
 
-// Byte offset of the correction-phase staging buffers (after the pseudo tiles,
-// the count, the bitmap and the dropped list).
+// LDS bytes of the correction phase: pseudo-K and pseudo-V tiles, the
+// dropped count, the kept-block bitmap and the dropped-block list.
 template <int D, int BLK, bool F8>
-__host__ __device__ constexpr int corr_stage_offset(int nkb) {
-  return ((2 * Cfg<D, BLK, F8>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb + 1023) / 1024) * 1024;
+__host__ __device__ constexpr int corr_lds_bytes(int nkb) {
+  return 2 * Cfg<D, BLK, F8>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb;
 }
 
 // LDS transpose reads.  The K/V tiles a block reads were completed by an
@@ -388,7 +387,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
       float x = __builtin_fmaf(S[r], sc, -mb);
       if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
-      if (mode == 2 && kic >= nvalid) x = -INFINITY;
+      if (mode == 2 && kc * 32 + kic >= nvalid) x = -INFINITY;
       const float p = __builtin_amdgcn_exp2f(x);
       sum += p;
       pk[r >> 3][r & 7] = (__bf16)p;
@@ -707,13 +706,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     }
 
     // ---- mean correction: dropped blocks as pseudo-keys
-    // LDS during this phase: pseudo-K tile (32 rows, bf16) | pseudo-V tile |
-    // ndrop | kept-block bitmap | dropped-block list | 2 staging buffers of
-    // the fp32 kbar/vbar rows of a 32-pseudo-key chunk (global_load_lds,
-    // one chunk ahead of the compute).  In fp8 the pseudo rows are divided
-    // by the head's k / v scale so that they share the code units of the
-    // fp8 K and V (the logit scale cs and the output scale v_s then apply
-    // to both), and Q is widened to bf16 (exact for e4m3 values).
+    // LDS during this phase: pseudo-K tile (BLK rows, bf16) | pseudo-V tile |
+    // ndrop | kept-block bitmap | dropped-block list.  The dropped blocks are
+    // gathered BLK at a time: each thread loads its share of their fp32
+    // kbar/vbar rows with plain loads (TPP issued before any is converted)
+    // and writes them as bf16 into the padded tiles, which are then taken 32
+    // pseudo-keys at a time.  In
+    // fp8 the pseudo rows are divided by the head's k / v scale so that they
+    // share the code units of the fp8 K and V (the logit scale cs and the
+    // output scale v_s then apply to both), and Q is widened to bf16 (exact
+    // for e4m3 values).
     if (a.sparse && a.mean_correction && i > 0) {
       __syncthreads();
       char* pk_t = lds;
@@ -722,7 +724,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       uint32_t* bm = (uint32_t*)(ndrop_slot + 1);
       const int nwords = (i + 31) >> 5;
       int* drop = (int*)(bm + nwords);
-      char* stage = lds + corr_stage_offset<D, BLK, F8>(a.seq.nkb_stride);
       for (int w = tid; w < nwords; w += nthr) bm[w] = 0u;
       __syncthreads();
       for (int n = tid; n < nblk; n += nthr) {
@@ -773,42 +774,51 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
             }
           }
       }
-      // stage chunk c (32 rows of kbar then 32 rows of vbar, fp32) into buffer bb
-      auto stage_load = [&](int c0, int bb) __attribute__((always_inline)) {
-        constexpr int LPR = D * 4 / 16;        // lanes per fp32 row
-        constexpr int RPO = 64 / LPR;          // rows per wave op
-        for (int it = wave; it < 64 / RPO; it += nwaves) {
-          const int rr = it * RPO + lane / LPR;   // 0..63: K rows then V rows
-          const int r32 = rr & 31;
-          const int id = c0 + r32 < ndrop ? drop[c0 + r32] : 0;
-          const float* src = (rr < 32 ? kbr : vbr) + (long)id * D + (lane % LPR) * 4;
-          __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(stage + bb * C::STG + it * 1024), 16, 0,
-                                           0);
+      constexpr int CH8 = D / 8;              // 8-element pieces per row
+      constexpr int TASKS = 2 * BLK * CH8;    // pieces of a round (K rows, then V rows)
+      constexpr int TPP = 4;                  // pieces per thread held in registers at once
+      for (int c0 = 0; c0 < ndrop; c0 += BLK) {
+        for (int base = 0; base < TASKS; base += nthr * TPP) {
+          float4 x[TPP][2];
+#pragma unroll
+          for (int u = 0; u < TPP; ++u) {
+            const int task = base + u * nthr + tid;
+            if (task < TASKS) {
+              const int rr = task / CH8;        // 0 .. 2*BLK-1: K rows then V rows
+              const int c = task - rr * CH8;
+              const int pidx = c0 + (rr & (BLK - 1));
+              const int id = drop[pidx < ndrop ? pidx : 0];  // past the end: any finite row (masked)
+              const float* src = (rr < BLK ? kbr : vbr) + (long)id * D + c * 8;
+              x[u][0] = *(const float4*)src;
+              x[u][1] = *(const float4*)(src + 4);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < TPP; ++u) {
+            const int task = base + u * nthr + tid;
+            if (task < TASKS) {
+              const int rr = task / CH8;
+              const int c = task - rr * CH8;
+              const float f = rr < BLK ? kmul : vmul;
+              const uint4 w = make_uint4(pack_bf16x2(x[u][0].x * f, x[u][0].y * f),
+                                         pack_bf16x2(x[u][0].z * f, x[u][0].w * f),
+                                         pack_bf16x2(x[u][1].x * f, x[u][1].y * f),
+                                         pack_bf16x2(x[u][1].z * f, x[u][1].w * f));
+              *(uint4*)((rr < BLK ? pk_t : pv_t) + (rr & (BLK - 1)) * C::RS16 + c * 16) = w;
+            }
+          }
         }
-      };
-      constexpr int CH8 = D / 8;  // 8-element pieces per row
-      if (ndrop > 0) stage_load(0, 0);
-      for (int c0 = 0, cc = 0; c0 < ndrop; c0 += 32, ++cc) {
-        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (c0 + 32 < ndrop) stage_load(c0 + 32, (cc + 1) & 1);
-        const char* sb = stage + (cc & 1) * C::STG;
-        for (int task = tid; task < 2 * 32 * CH8; task += nthr) {
-          const int rr = task / CH8;            // 0..63
-          const int c = task - rr * CH8;
-          const float f = rr < 32 ? kmul : vmul;
-          const float4 x0 = *(const float4*)(sb + rr * D * 4 + c * 32);
-          const float4 x1 = *(const float4*)(sb + rr * D * 4 + c * 32 + 16);
-          const uint4 w = make_uint4(pack_bf16x2(x0.x * f, x0.y * f), pack_bf16x2(x0.z * f, x0.w * f),
-                                     pack_bf16x2(x1.x * f, x1.y * f), pack_bf16x2(x1.z * f, x1.w * f));
-          *(uint4*)((rr < 32 ? pk_t : pv_t) + (rr & 31) * C::RS16 + c * 16) = w;
+        const int nv = min(BLK, ndrop - c0);
+#pragma unroll 1
+        for (int cc = 0; cc * 32 < nv; ++cc) {
+          if constexpr (F8) {
+            run_tile(pk_t + cc * 32 * C::RS16, pv_t + cc * 32 * C::RS16, 1, 2, nv - cc * 32, bias, q16, 0);
+          } else {
+            run_tile(pk_t + cc * 32 * C::RS16, pv_t + cc * 32 * C::RS16, 1, 2, nv - cc * 32, bias, qop, 0);
+          }
         }
         __syncthreads();
-        if constexpr (F8) {
-          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, q16, 0);
-        } else {
-          run_tile(pk_t, pv_t, 1, 2, min(32, ndrop - c0), bias, qop, 0);
-        }
       }
     }
 
@@ -941,7 +951,7 @@ template <int D, int BLK, bool F8>
 static size_t attn_lds_bytes(int nkb) {
   using C = Cfg<D, BLK, F8>;
   size_t lds = 4 * (size_t)C::TILE;
-  const size_t corr = (size_t)corr_stage_offset<D, BLK, F8>(nkb) + 2 * (size_t)C::STG;
+  const size_t corr = (size_t)corr_lds_bytes<D, BLK, F8>(nkb);
   return corr > lds ? corr : lds;
 }
 
