@@ -77,6 +77,9 @@ struct Cfg {
   static constexpr int NLD = TILE / 1024;      // global_load_lds wave ops per tile
   static constexpr int RS16 = 2 * D + (D == 128 ? 32 : 16);  // bf16 pseudo-key rows
   static constexpr int PSB = BLK * RS16;       // one pseudo-key tile of BLK rows (bf16)
+  static constexpr int NPW = (NLD + 3) / 4;    // copy ops per wave and tile with 4 waves
+  static constexpr int NPWP = (NPW + 3) & ~3;  // table entries per thread (16-byte rows)
+  static constexpr int DTAB = NPWP * 256 * 4;  // LDS bytes of the copy-offset table
 };
 
 // LDS bytes of the correction phase: pseudo-K and pseudo-V tiles, the
@@ -98,6 +101,8 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* __restrict__ p) {
 __device__ __forceinline__ i32x2 lds_read_tr8(const char* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)p);
 }
+
+__device__ __forceinline__ u32x4 lds_read_u32x4(const unsigned* __restrict__ p) { return *(const u32x4*)p; }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = __lane_id();
@@ -333,9 +338,54 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   auto dma_rest = [&]() __attribute__((always_inline)) {
     while (dq_it < C::NLD) dma_step();
   };
+  // Contiguous caches with 4 waves: for every full key block the lane
+  // offsets of a wave's copies (relative to the block's first row) are the
+  // same, so they are computed once per tile into an LDS table (thread tid's
+  // entries at dtab[NPWP tid, +NPWP), read back with 16-byte loads before the
+  // first copy is issued) and each copy of a full block is a wave-uniform base
+  // plus that 32-bit offset.  Paged caches and a sequence's last, partial
+  // block take the cursor above.  Copy op k of the wave exists for every wave
+  // when k < NLD / 4.
+  const bool dfast = !ptab && nwaves == 4;
+  unsigned* const dtab = (unsigned*)(smem + a.lds_dtab) + C::NPWP * tid;
+  if (dfast) {
+#pragma unroll
+    for (int k = 0; k < C::NPW; ++k) {
+      const int it = wave + 4 * k;
+      if (k < C::NLD / 4 || it < C::NLD) {
+        const int o = 1024 * it + 16 * lane;
+        const int row = o / C::RS, byte = o - row * C::RS;
+        const bool inrow = byte < C::ROWB && row < BLK;
+        dtab[k] = (unsigned)(min(row, BLK - 1) * rowbytes + (inrow ? byte : 0));
+      }
+    }
+  }
+  auto issue_fast = [&](int j, int bb) __attribute__((always_inline)) {
+    const long b0 = ((long)s * a.seq.seqlen_k + (long)j * BLK) * rowbytes + h * C::ROWB;
+    const char* kb = (const char*)a.kv.k + b0;
+    const char* vb = (const char*)a.kv.v + b0;
+    u32x4 offv[C::NPWP / 4];
+#pragma unroll
+    for (int r = 0; r < C::NPWP / 4; ++r) offv[r] = lds_read_u32x4(dtab + 4 * r);
+#pragma unroll
+    for (int k = 0; k < C::NPW; ++k) {
+      const int it = wave + 4 * k;
+      if (k < C::NLD / 4 || it < C::NLD) {
+        const unsigned off = offv[k >> 2][k & 3];
+        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((const void*)(vb + off), (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024),
+                                         16, 0, 0);
+      }
+    }
+  };
   auto issue_load = [&](int j, int bb, int pids) __attribute__((always_inline)) {
-    dma_begin(j, bb, pids);
-    dma_rest();
+    if (dfast && (j + 1) * BLK <= g.Sk) {
+      issue_fast(j, bb);
+    } else {
+      dma_begin(j, bb, pids);
+      dma_rest();
+    }
   };
 
   // ===================== bf16 operand path (32x32x16 MFMA) =================
@@ -946,13 +996,20 @@ void attn_kernel(AttnArgs a) {
   }
 }
 
-// LDS bytes the attention kernel needs for a given key-block count.
+// LDS of the attention kernel for a given key-block count: the K/V tiles or
+// the correction phase's buffers (whichever is larger), then the copy-offset
+// table (then, at launch, the next-tile broadcast slots).
 template <int D, int BLK, bool F8>
-static size_t attn_lds_bytes(int nkb) {
+static size_t attn_lds_dtab(int nkb) {
   using C = Cfg<D, BLK, F8>;
   size_t lds = 4 * (size_t)C::TILE;
   const size_t corr = (size_t)corr_lds_bytes<D, BLK, F8>(nkb);
   return corr > lds ? corr : lds;
+}
+
+template <int D, int BLK, bool F8>
+static size_t attn_lds_bytes(int nkb) {
+  return attn_lds_dtab<D, BLK, F8>(nkb) + Cfg<D, BLK, F8>::DTAB;
 }
 
 static int compute_units() {
@@ -984,6 +1041,7 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   AttnArgs a = a0;
   a.ntiles = (int)ntiles;
   a.sched_slot = (int)(g_slot_counter.fetch_add(1) % kSchedSlots);
+  a.lds_dtab = (int)attn_lds_dtab<D, BLK, F8>(a0.seq.nkb_stride);
   a.lds_sched = (int)lds;
   const long grid = ntiles < compute_units() ? ntiles : compute_units();
   hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, st, a.sched_slot);

@@ -91,6 +91,7 @@ struct AttnArgs {
   int ntiles;               // Hkv * batch * parts * nqb_grid
   int sched_slot;           // tile-scheduler counter slot of this launch
   int lds_sched;            // LDS byte offset of the next-tile broadcast
+  int lds_dtab;             // LDS byte offset of the copy-offset table
 };
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t s);
