@@ -338,15 +338,18 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   auto dma_rest = [&]() __attribute__((always_inline)) {
     while (dq_it < C::NLD) dma_step();
   };
-  // Contiguous caches with 4 waves: for every full key block the lane
-  // offsets of a wave's copies (relative to the block's first row) are the
-  // same, so they are computed once per tile into an LDS table (thread tid's
+  // With 4 waves, the lane offsets of a wave's copies are the same for every
+  // full key block, relative to the block's first row (contiguous caches) or
+  // to the first row of the page that holds the op (paged caches whose pages
+  // fill a whole number of 1 KB copy ops in LDS, so that no op straddles two
+  // pages).  They are computed once per tile into an LDS table (thread tid's
   // entries at dtab[NPWP tid, +NPWP), read back with 16-byte loads before the
   // first copy is issued) and each copy of a full block is a wave-uniform base
-  // plus that 32-bit offset.  Paged caches and a sequence's last, partial
-  // block take the cursor above.  Copy op k of the wave exists for every wave
-  // when k < NLD / 4.
-  const bool dfast = !ptab && nwaves == 4;
+  // plus that 32-bit offset.  Other paged layouts and a sequence's last,
+  // partial block take the cursor above.  Copy op k of the wave exists for
+  // every wave when k < NLD / 4.
+  const bool dfast = nwaves == 4 && (!ptab || ((C::RS << plog) & 1023) == 0);
+  const int rowmask = ptab ? (1 << plog) - 1 : BLK - 1;
   unsigned* const dtab = (unsigned*)(smem + a.lds_dtab) + C::NPWP * tid;
   if (dfast) {
 #pragma unroll
@@ -356,14 +359,12 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
         const int o = 1024 * it + 16 * lane;
         const int row = o / C::RS, byte = o - row * C::RS;
         const bool inrow = byte < C::ROWB && row < BLK;
-        dtab[k] = (unsigned)(min(row, BLK - 1) * rowbytes + (inrow ? byte : 0));
+        dtab[k] = (unsigned)((min(row, BLK - 1) & rowmask) * rowbytes + (inrow ? byte : 0));
       }
     }
   }
-  auto issue_fast = [&](int j, int bb) __attribute__((always_inline)) {
-    const long b0 = ((long)s * a.seq.seqlen_k + (long)j * BLK) * rowbytes + h * C::ROWB;
-    const char* kb = (const char*)a.kv.k + b0;
-    const char* vb = (const char*)a.kv.v + b0;
+  auto issue_fast = [&](int j, int bb, int pids) __attribute__((always_inline)) {
+    const long b0 = ptab ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + (long)j * BLK) * rowbytes + h * C::ROWB;
     u32x4 offv[C::NPWP / 4];
 #pragma unroll
     for (int r = 0; r < C::NPWP / 4; ++r) offv[r] = lds_read_u32x4(dtab + 4 * r);
@@ -371,17 +372,22 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     for (int k = 0; k < C::NPW; ++k) {
       const int it = wave + 4 * k;
       if (k < C::NLD / 4 || it < C::NLD) {
+        long pb = b0;
+        if (ptab) {  // page of the op's first row (every row of the op is in it)
+          const int pi = min((1024 * it) / C::RS, BLK - 1) >> plog;
+          pb += ((long)__builtin_amdgcn_readlane(pids, pi) << plog) * rowbytes;
+        }
         const unsigned off = offv[k >> 2][k & 3];
-        __builtin_amdgcn_global_load_lds((const void*)(kb + off), (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0,
-                                         0);
-        __builtin_amdgcn_global_load_lds((const void*)(vb + off), (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)a.kv.k + pb + off),
+                                         (lds_void*)(lds + bb * C::TILE + it * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const char*)a.kv.v + pb + off),
+                                         (lds_void*)(lds + (2 + bb) * C::TILE + it * 1024), 16, 0, 0);
       }
     }
   };
   auto issue_load = [&](int j, int bb, int pids) __attribute__((always_inline)) {
     if (dfast && (j + 1) * BLK <= g.Sk) {
-      issue_fast(j, bb);
+      issue_fast(j, bb, pids);
     } else {
       dma_begin(j, bb, pids);
       dma_rest();

@@ -14,8 +14,13 @@ from tests.helpers import (BF16_MAX_ABS, BF16_REL_L2, assert_mask_matches, f64, 
 pytestmark = pytest.mark.gpu
 
 
-def test_paged_matches_oracle_and_contiguous(gpu):
-    hq, hkv, d, b, page = 8, 2, 128, 128, 64
+# page sizes on both copy paths: pages that fill whole 1 KB LDS copy ops
+# (at least 32 rows for d = 128 in bf16, 64 for d = 64) take the per-tile
+# offset table, smaller ones the per-copy cursor
+@pytest.mark.parametrize("d,b,page", [(128, 128, 64), (128, 128, 16), (128, 128, 32), (128, 128, 128), (64, 64, 16),
+                                      (64, 64, 64)])
+def test_paged_matches_oracle_and_contiguous(gpu, d, b, page):
+    hq, hkv = 8, 2
     kv_lens = [700, 1500, 2048, 333]
     q_lens = [700, 300, 1024, 333]
     print(f"[case] paged kv_lens={kv_lens} q_lens={q_lens} hq={hq} hkv={hkv} d={d} b={b} page={page}", flush=True)
