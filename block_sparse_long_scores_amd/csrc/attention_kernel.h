@@ -437,18 +437,22 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       __attribute__((always_inline)) {
     const float mb = mref[nt] - bias;
     const float sc = F8 ? cs[nt] : a.scale_log2;
-    float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
       float x = __builtin_fmaf(S[r], sc, -mb);
       if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
       if (mode == 2 && kc * 32 + kic >= nvalid) x = -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(x);
-      sum += p;
-      pk[r >> 3][r & 7] = (__bf16)p;
+      pk[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
     }
-    lsum[nt] += sum;
+    // The row sum adds the bf16-rounded P that the P V MFMA weights V with,
+    // two values per v_dot2c_f32_bf16 (fp32 accumulate, times 1.0).
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bf16x2 pr = {pk[e >> 2][2 * (e & 3)], pk[e >> 2][2 * (e & 3) + 1]};
+      lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[nt], false);
+    }
   };
   auto pv = [&](const bf16x8 (&vop)[C::MT][2], const bf16x8 (&pk)[2], int nt) __attribute__((always_inline)) {
 #pragma unroll
@@ -466,6 +470,20 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);  // VALU
     }
   };
+  // The same for the bf16 chunk stages, with the stage's LDS operand reads
+  // placed first (they feed the next chunk's QK or P V) and each MFMA
+  // followed by one exp (a transcendental, its own scheduling class) and
+  // NV other VALU ops, which keeps every gap between MFMAs under one MFMA's
+  // issue time.
+  auto interleave2 = [&](auto nds, int nmfma, auto nv) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, decltype(nds)::value, 0);  // DS read
+    for (int k = 0; k < nmfma; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, decltype(nv)::value, 0);  // VALU or TRANS
+    }
+  };
+  using V4 = std::integral_constant<int, 4>;
+  using V8 = std::integral_constant<int, 8>;
   using V5 = std::integral_constant<int, 5>;
   using V16 = std::integral_constant<int, 16>;
 
@@ -503,14 +521,14 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       softmax(S[cp][0], 0, c, mode, nvalid, bias, p0);
       if (more) S[np][0] = qk(kop, qq[0]);
       if (c > 0) pv(vop[np], p1[np], 1);
-      interleave(c > 0 ? 2 * C::KS : C::KS, V5{});
+      interleave2(std::integral_constant<int, C::KS>{}, c > 0 ? 2 * C::KS : C::KS, V4{});
       __builtin_amdgcn_sched_barrier(0);
       // stage 2
       if (more) load_vop(vbase, c + 1, vop[np]);
       softmax(S[cp][1], 1, c, mode, nvalid, bias, p1[cp]);
       if (more) S[np][1] = qk(kop, qq[1]);
       pv(vop[cp], p0, 0);
-      interleave(C::KS + 2 * C::MT, V5{});
+      interleave2(std::integral_constant<int, 4 * C::MT>{}, C::KS + 2 * C::MT, V4{});
       __builtin_amdgcn_sched_barrier(0);
     }
     const int lp = (nch - 1) & 1;
