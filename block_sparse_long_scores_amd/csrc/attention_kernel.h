@@ -437,22 +437,20 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       __attribute__((always_inline)) {
     const float mb = mref[nt] - bias;
     const float sc = F8 ? cs[nt] : a.scale_log2;
+    // (The row sum stays in fp32 VALU adds: v_dot2c_f32_bf16 on the packed P
+    // would halve them, but a dot instruction waits for the MFMA in flight.)
+    float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
       float x = __builtin_fmaf(S[r], sc, -mb);
       if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
       if (mode == 2 && kc * 32 + kic >= nvalid) x = -INFINITY;
-      pk[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(x);
+      const float p = __builtin_amdgcn_exp2f(x);
+      sum += p;
+      pk[r >> 3][r & 7] = (__bf16)p;
     }
-    // The row sum adds the bf16-rounded P that the P V MFMA weights V with,
-    // two values per v_dot2c_f32_bf16 (fp32 accumulate, times 1.0).
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bf16x2 pr = {pk[e >> 2][2 * (e & 3)], pk[e >> 2][2 * (e & 3) + 1]};
-      lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[nt], false);
-    }
+    lsum[nt] += sum;
   };
   auto pv = [&](const bf16x8 (&vop)[C::MT][2], const bf16x8 (&pk)[2], int nt) __attribute__((always_inline)) {
 #pragma unroll
@@ -487,10 +485,52 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   using V5 = std::integral_constant<int, 5>;
   using V16 = std::integral_constant<int, 16>;
 
+  // One pipeline stage, written in issue order: the P V MFMAs of one column
+  // set first (operands in registers), then the QK chain of the next chunk
+  // (its K operand, read at the start of the chunk, arrives meanwhile); after
+  // every MFMA slot the softmax of the next score(s) of the other column set
+  // (fma, exp2, add; every second score the bf16 pair convert), so that each
+  // gap between MFMAs holds a few VALU ops that issue under the MFMA in
+  // flight.  Scores are tied to slots statically, whether or not the slot's
+  // MFMA exists in this stage.
+  auto stage_mix = [&](const f32x16& Sin, int nts, int kc, int mode, int nvalid, float bias, bf16x8 (&pk)[2],
+                       bool pv_on, const bf16x8 (&vv)[C::MT][2], const bf16x8 (&pp)[2], int ntp, bool qk_on,
+                       const bf16x8 (&kk)[C::KS], const bf16x8 (&qs)[C::KS], f32x16& Sout)
+      __attribute__((always_inline)) {
+    constexpr int NPV = 2 * C::MT, NSLOT = NPV + C::KS, PER = 16 / NSLOT;
+    const float mb = mref[nts] - bias;
+    const float sc = F8 ? cs[nts] : a.scale_log2;
+    float sum = 0.f;
+    float ph[16];
+#pragma unroll
+    for (int g = 0; g < NSLOT; ++g) {
+      if (g < NPV) {
+        if (pv_on) O[g >> 1][ntp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[g >> 1][g & 1], pp[g & 1], O[g >> 1][ntp], 0, 0, 0);
+      } else if (qk_on) {
+        Sout = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[g - NPV], qs[g - NPV], g == NPV ? f32x16{} : Sout, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int r = g * PER + e;
+        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+        float x = __builtin_fmaf(Sin[r], sc, -mb);
+        if (mode == 1 && kc * 32 + kic > rib[nts]) x = -INFINITY;
+        if (mode == 2 && kc * 32 + kic >= nvalid) x = -INFINITY;
+        ph[r] = __builtin_amdgcn_exp2f(x);
+        sum += ph[r];
+        if (r & 1) {
+          pk[r >> 3][(r & 7) - 1] = (__bf16)ph[r - 1];
+          pk[r >> 3][r & 7] = (__bf16)ph[r];
+        }
+      }
+    }
+    lsum[nts] += sum;
+  };
+
   // The NCH 32-key chunks of one bf16 K/V tile (or of one pseudo-key tile),
   // software-pipelined in two stages per chunk c:
-  //   stage 1: softmax(S_c, columns 0)  ||  QK(c+1, columns 0), PV(c-1, columns 1)
-  //   stage 2: softmax(S_c, columns 1)  ||  QK(c+1, columns 1), PV(c, columns 0)
+  //   stage 1: PV(c-1, columns 1), QK(c+1, columns 0)  ||  softmax(S_c, columns 0)
+  //   stage 2: PV(c, columns 0), QK(c+1, columns 1)    ||  softmax(S_c, columns 1)
   // so the exp/sum/convert VALU work of one column set runs under the MFMAs of
   // the other; PV(last, columns 1) closes the tile.  Operand buffers are
   // indexed by chunk parity (no register copies after unrolling), and the
@@ -518,17 +558,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       if (more) load_kop(kbase, c + 1, kop);
       dma_some(dq);
       // stage 1
-      softmax(S[cp][0], 0, c, mode, nvalid, bias, p0);
-      if (more) S[np][0] = qk(kop, qq[0]);
-      if (c > 0) pv(vop[np], p1[np], 1);
-      interleave2(std::integral_constant<int, C::KS>{}, c > 0 ? 2 * C::KS : C::KS, V4{});
+      stage_mix(S[cp][0], 0, c, mode, nvalid, bias, p0, c > 0, vop[np], p1[np], 1, more, kop, qq[0], S[np][0]);
+      interleave2(std::integral_constant<int, C::KS>{}, (c > 0 ? 2 * C::MT : 0) + (more ? C::KS : 0), V4{});
       __builtin_amdgcn_sched_barrier(0);
       // stage 2
       if (more) load_vop(vbase, c + 1, vop[np]);
-      softmax(S[cp][1], 1, c, mode, nvalid, bias, p1[cp]);
-      if (more) S[np][1] = qk(kop, qq[1]);
-      pv(vop[cp], p0, 0);
-      interleave2(std::integral_constant<int, 4 * C::MT>{}, C::KS + 2 * C::MT, V4{});
+      stage_mix(S[cp][1], 1, c, mode, nvalid, bias, p1[cp], true, vop[cp], p0, 0, more, kop, qq[1], S[np][1]);
+      interleave2(std::integral_constant<int, 4 * C::MT>{}, 2 * C::MT + (more ? C::KS : 0), V4{});
       __builtin_amdgcn_sched_barrier(0);
     }
     const int lp = (nch - 1) & 1;
