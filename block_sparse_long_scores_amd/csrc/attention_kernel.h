@@ -89,6 +89,36 @@ __host__ __device__ constexpr int corr_lds_bytes(int nkb) {
   return 2 * Cfg<D, BLK, F8>::PSB + 4 + 4 * ((nkb + 31) / 32) + 4 * nkb;
 }
 
+// fp8 S^T chunk (32 keys x 32 queries, K on the A side) as a chain of
+// v_mfma_f32_32x32x64_f8f6f4 (e4m3 A and B, no block scale) with the
+// accumulator in VGPRs, where the softmax reads it (a compiler-placed result
+// would land in AGPRs next to the O^T accumulators and need a copy per
+// register).  Hazards the compiler cannot see through the asm are covered
+// inside it: 2 wait states before the first MFMA (VALU write -> MFMA source
+// read) and 20 after the last (16-pass MFMA result -> VALU access).
+__device__ __forceinline__ f32x16 qk8_chain(const i32x8 (&k)[2], const i32x8 (&q)[2]) {
+  f32x16 S;
+  asm("s_nop 1\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %0, %1, %3, 0\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %0, %2, %4, %0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3"
+      : "=&v"(S)
+      : "v"(k[0]), "v"(k[1]), "v"(q[0]), "v"(q[1]));
+  return S;
+}
+
+__device__ __forceinline__ f32x16 qk8_chain(const i32x8 (&k)[1], const i32x8 (&q)[1]) {
+  f32x16 S;
+  asm("s_nop 1\n\t"
+      "v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3"
+      : "=&v"(S)
+      : "v"(k[0]), "v"(q[0]));
+  return S;
+}
+
 // LDS transpose reads.  The K/V tiles a block reads were completed by an
 // explicit s_waitcnt + barrier at the start of that block, while the copies
 // in flight during it fill the other buffer.  The restrict-qualified pointer
@@ -612,11 +642,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   };
   auto qk8 = [&](const i32x8 (&kop)[C::KS8], int nt) __attribute__((always_inline)) -> f32x16 {
     f32x16 S = f32x16{};
-    if constexpr (F8) {
-#pragma unroll
-      for (int ks = 0; ks < C::KS8; ++ks)
-        S = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[ks], qop[nt][ks], S, 0, 0, 0, 0, 0, 0);
-    }
+    if constexpr (F8) S = qk8_chain(kop, qop[nt]);
     return S;
   };
   // Superchunk softmax of column set nt: Sn[q] is the S^T chunk 2sc + q.
