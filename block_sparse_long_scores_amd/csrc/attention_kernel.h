@@ -119,6 +119,21 @@ __device__ __forceinline__ f32x16 qk8_chain(const i32x8 (&k)[1], const i32x8 (&q
   return S;
 }
 
+// The same chain split into one asm statement per MFMA, so that the
+// compiler can issue independent VALU work between them: the first writes
+// S (C = 0), the last accumulates into it and carries the 20 wait states
+// after which the VALU may read S.  Nothing may touch S between the two
+// (the second MFMA reads it as its exactly overlapping accumulator, which
+// needs no wait states).
+__device__ __forceinline__ void qk8_first(f32x16& S, const i32x8& k, const i32x8& q) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(S) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void qk8_last(f32x16& S, const i32x8& k, const i32x8& q) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3"
+               : "+v"(S)
+               : "v"(k), "v"(q));
+}
+
 // LDS transpose reads.  The K/V tiles a block reads were completed by an
 // explicit s_waitcnt + barrier at the start of that block, while the copies
 // in flight during it fill the other buffer.  The restrict-qualified pointer
@@ -645,47 +660,40 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     if constexpr (F8) S = qk8_chain(kop, qop[nt]);
     return S;
   };
-  // Superchunk softmax of column set nt: Sn[q] is the S^T chunk 2sc + q.
-  // mode 1 applies the causal mask (diagonal block).
-  auto softmax8 = [&](f32x16 (&Sn)[2], int nt, int sc, int mode, i32x8& pk, int& sbyte)
+  // Superchunk softmax of column set nt (Sn[q] is the S^T chunk 2sc + q), in
+  // pieces: sm8_scale(q) applies the causal mask (mode 1) to chunk q and
+  // takes its max and power-of-two scale; sm8_exp(q, j) turns registers
+  // 4j..4j+3 of chunk q into 4 scaled e4m3 bytes of P.
+  auto sm8_scale = [&](f32x16 (&Sn)[2], int q, int nt, int sc, int mode, int (&bq)[2], float (&bias)[2])
       __attribute__((always_inline)) {
-    float bias[2];
-    int bq[2];
+    if (mode == 1) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (mode == 1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-          if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
-        }
-      }
-      // NaN-propagating maximum (v_maximum3_f32): no canonicalizing copies of
-      // the MFMA results, which fmaxf needs in IEEE mode
-      float m = __builtin_elementwise_maximum(Sn[q][0], Sn[q][1]);
-#pragma unroll
-      for (int r = 2; r < 16; r += 2)
-        m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(Sn[q][r], Sn[q][r + 1]));
-      m = __builtin_elementwise_maximum(m, partner32(m));
-      float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
-      fx = fminf(fmaxf(fx, -110.f), 120.f);
-      bq[q] = (int)fx - 7;
-      bias[q] = mref[nt] + (float)bq[q];
-    }
-    sbyte = 127 + (hh ? bq[1] : bq[0]);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias[q]));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias[q]));
-        const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias[q]));
-        const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias[q]));
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-        pk[4 * q + j] = w;
+      for (int r = 0; r < 16; ++r) {
+        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+        if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
       }
     }
+    // NaN-propagating maximum (v_maximum3_f32): no canonicalizing copies of
+    // the MFMA results, which fmaxf needs in IEEE mode
+    float m = __builtin_elementwise_maximum(Sn[q][0], Sn[q][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2)
+      m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(Sn[q][r], Sn[q][r + 1]));
+    m = __builtin_elementwise_maximum(m, partner32(m));
+    float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
+    fx = fminf(fmaxf(fx, -110.f), 120.f);
+    bq[q] = (int)fx - 7;
+    bias[q] = mref[nt] + (float)bq[q];
+  };
+  auto sm8_exp = [&](const f32x16 (&Sn)[2], int q, int j, int nt, const float (&bias)[2], i32x8& pk)
+      __attribute__((always_inline)) {
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias[q]));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias[q]));
+    const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias[q]));
+    const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias[q]));
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+    pk[4 * q + j] = w;
   };
   const i32x8 ones8 = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
                             0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
@@ -697,12 +705,59 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       Lacc[nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pk, Lacc[nt], 0, 0, 0, 127, 0, sbyte);
     }
   };
+  // One fp8 stage in issue order, each slot pinned by a scheduling barrier:
+  // the P V MFMAs of column set ntp (its O tiles, then the row-sum MFMA),
+  // then the two QK chains of column set ntq (first MFMAs, then last ones);
+  // after each slot one piece of the softmax of column set nts (the two
+  // scales first, then the eight 4-score groups).
+  auto stage8 = [&](f32x16 (&Sn)[2], int nts, int sc, int mode, i32x8& pk, int& sbyte, bool pv_on,
+                    const i32x8 (&vv)[C::MT], const i32x8& pp, int psb, int ntp, bool qk_on,
+                    const i32x8 (&k0)[C::KS8], const i32x8 (&k1)[C::KS8], int ntq, f32x16 (&So)[2])
+      __attribute__((always_inline)) {
+    constexpr int NPVS = C::MT + 1, NSLOT = NPVS + 2 * C::KS8, NPIECE = 10;
+    int bq[2];
+    float bias[2];
+#pragma unroll
+    for (int g = 0; g < NSLOT; ++g) {
+      if constexpr (F8) {
+        if (g < C::MT) {
+          if (pv_on)
+            O[g][ntp] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv[g], pp, O[g][ntp], 0, 0, 0, 127, 0, psb);
+        } else if (g == C::MT) {
+          if (pv_on) Lacc[ntp] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pp, Lacc[ntp], 0, 0, 0, 127, 0, psb);
+        } else if (qk_on) {
+          const int t = g - NPVS;
+          if constexpr (C::KS8 == 2) {
+            if (t == 0) qk8_first(So[0], k0[0], qop[ntq][0]);
+            if (t == 1) qk8_first(So[1], k1[0], qop[ntq][0]);
+            if (t == 2) qk8_last(So[0], k0[1], qop[ntq][1]);
+            if (t == 3) qk8_last(So[1], k1[1], qop[ntq][1]);
+          } else {
+            if (t == 0) So[0] = qk8(k0, ntq);
+            if (t == 1) So[1] = qk8(k1, ntq);
+          }
+        }
+      }
+#pragma unroll
+      for (int pc = 0; pc < NPIECE; ++pc) {
+        if ((pc < NSLOT ? pc : NSLOT - 1) == g) {
+          if (pc < 2) {
+            sm8_scale(Sn, pc, nts, sc, mode, bq, bias);
+          } else {
+            sm8_exp(Sn, (pc - 2) >> 2, (pc - 2) & 3, nts, bias, pk);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sbyte = 127 + (hh ? bq[1] : bq[0]);
+  };
   // The NSC superchunks of one fp8 K/V tile, two stages per superchunk sc:
-  //   stage X: softmax(S_sc, columns 0) || QK(sc, columns 1), PV(sc-1, columns 1)
-  //   stage Y: softmax(S_sc, columns 1) || PV(sc, columns 0), QK(sc+1, columns 0)
+  //   stage X: PV(sc-1, columns 1), QK(sc, columns 1)    ||  softmax(S_sc, columns 0)
+  //   stage Y: PV(sc, columns 0),   QK(sc+1, columns 0)  ||  softmax(S_sc, columns 1)
   // so that only two S sets (one per column set) are ever live.  The K
-  // operands of superchunk sc+1 are read at the start of stage Y, behind the
-  // PV MFMAs; the V operands are double-buffered by superchunk parity.
+  // operands of superchunk sc+1 are read at the start of stage Y, behind its
+  // P V MFMAs; the V operands are double-buffered by superchunk parity.
   auto run_tile8 = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
     const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
     const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
@@ -724,25 +779,15 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       // stage X
       load_vop8(vbase, sc, vop[cp]);
       dma_some(dq);
-      softmax8(S0, 0, sc, mode, pp0, sb0);
-      S1[0] = qk8(kop[0], 1);
-      S1[1] = qk8(kop[1], 1);
-      if (sc > 0) pv8(vop[cp ^ 1], pp1, sb1, 1);
-      interleave(2 * C::KS8 + (sc > 0 ? C::MT + 1 : 0), V16{});
       __builtin_amdgcn_sched_barrier(0);
+      stage8(S0, 0, sc, mode, pp0, sb0, sc > 0, vop[cp ^ 1], pp1, sb1, 1, true, kop[0], kop[1], 1, S1);
       // stage Y
       if (more) {
         load_kop8(kbase, 2 * sc + 2, kop[0]);
         load_kop8(kbase, 2 * sc + 3, kop[1]);
       }
-      softmax8(S1, 1, sc, mode, pp1, sb1);
-      pv8(vop[cp], pp0, sb0, 0);
-      if (more) {
-        S0[0] = qk8(kop[0], 0);
-        S0[1] = qk8(kop[1], 0);
-      }
-      interleave(C::MT + 1 + (more ? 2 * C::KS8 : 0), V16{});
       __builtin_amdgcn_sched_barrier(0);
+      stage8(S1, 1, sc, mode, pp1, sb1, true, vop[cp], pp0, sb0, 0, more, kop[0], kop[1], 0, S0);
     }
     pv8(vop[(C::NSC - 1) & 1], pp1, sb1, 1);
   };
