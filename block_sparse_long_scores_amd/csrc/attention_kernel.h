@@ -673,13 +673,14 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
         if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
       }
     }
-    // NaN-propagating maximum (v_maximum3_f32): no canonicalizing copies of
-    // the MFMA results, which fmaxf needs in IEEE mode
-    float m = __builtin_elementwise_maximum(Sn[q][0], Sn[q][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2)
-      m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(Sn[q][r], Sn[q][r + 1]));
-    m = __builtin_elementwise_maximum(m, partner32(m));
+    // NaN-propagating maximum (v_maximum3_f32, no canonicalizing copies of
+    // the MFMA results, which fmaxf needs in IEEE mode): 16 values in 8 ops,
+    // then the other lane half's 16 keys of the same query column
+    const f32x16& v = Sn[q];
+    const float m0 = maximum3(v[0], v[1], v[2]), m1 = maximum3(v[3], v[4], v[5]);
+    const float m2 = maximum3(v[6], v[7], v[8]), m3 = maximum3(v[9], v[10], v[11]);
+    const float m4 = maximum3(v[12], v[13], v[14]);
+    const float m = max_partner32(maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), v[15]));
     float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
     fx = fminf(fmaxf(fx, -110.f), 120.f);
     bq[q] = (int)fx - 7;
@@ -691,7 +692,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias[q]));
     const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias[q]));
     const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias[q]));
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    // (the first convert's other half is overwritten by the second: x0's
+    // own register serves as its old value, no zeroing move)
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
     pk[4 * q + j] = w;
   };

@@ -68,4 +68,21 @@ __device__ __forceinline__ float partner32(float x) {
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
+// max(x, value of the lane 32 apart): the swap leaves the pair (own,
+// partner) in some order on every lane, so no lane select is needed.
+// NaN-propagating, like v_maximum_f32.
+__device__ __forceinline__ float max_partner32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// v_maximum3_f32 (NaN-propagating maximum of three).  In asm so that a
+// hand-balanced tree of them is kept as written: the compiler re-associates
+// nested maximum() calls into pairwise steps that cost more instructions.
+__device__ __forceinline__ float maximum3(float a, float b, float c) {
+  float r;
+  asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 }  // namespace fp2
