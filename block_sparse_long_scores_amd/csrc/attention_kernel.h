@@ -159,46 +159,6 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// S^T chunk = sum_ks K_ks Q_ks^T as a chain of v_mfma_f32_32x32x16_bf16 whose
-// accumulator stays in VGPRs (the O^T accumulators own the AGPR file, and the
-// compiler would otherwise place S in AGPRs as well and spill).  Hazards the
-// compiler cannot see through the asm are covered inside it: 2 wait states
-// before the first MFMA (VALU write -> MFMA source read) and 20 after the last
-// (MFMA result -> VALU read); a dependent MFMA chain on the same accumulator
-// needs none.
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[8], const bf16x8 (&q)[8]) {
-  f32x16 S;
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %9, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %10, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %11, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %12, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %5, %13, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %6, %14, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %7, %15, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %8, %16, %0\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3"
-      : "=&v"(S)
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]),
-        "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
-  return S;
-}
-
-__device__ __forceinline__ f32x16 qk_chain(const bf16x8 (&k)[4], const bf16x8 (&q)[4]) {
-  f32x16 S;
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %5, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-      "s_nop 15\n\t"
-      "s_nop 3"
-      : "=&v"(S)
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
-  return S;
-}
-
 // One tile: the G*b packed query rows of (sequence, KV head, query block) or
 // the 256-row part `part` of them, over its kept key blocks (or all blocks
 // j <= i when dense), then the mean correction and the epilogue.
@@ -827,7 +787,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       bf16x8 kop[C::KS];
       load_kop(lds, 0, kop);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) S0[nt] = qk_chain(kop, qop[nt]);
+      for (int nt = 0; nt < NT; ++nt) S0[nt] = qk(kop, qop[nt]);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
