@@ -435,28 +435,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     for (int ks = 0; ks < C::KS; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qq[ks], S, 0, 0, 0);
     return S;
   };
-  // P = exp2(S*cs - m + bias) as bf16 B-operands, row sums into lsum.
-  // mode 0: plain; 1: diagonal block (causal mask); 2: pseudo-keys (slots >=
-  // nvalid masked).  Key-in-chunk of accumulator register r: 8*(r/4) + 4*hh + r%4.
-  auto softmax = [&](const f32x16& S, int nt, int kc, int mode, int nvalid, float bias, bf16x8 (&pk)[2])
-      __attribute__((always_inline)) {
-    const float mb = mref[nt] - bias;
-    const float sc = F8 ? cs[nt] : a.scale_log2;
-    // (The row sum stays in fp32 VALU adds: v_dot2c_f32_bf16 on the packed P
-    // would halve them, but a dot instruction waits for the MFMA in flight.)
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-      float x = __builtin_fmaf(S[r], sc, -mb);
-      if (mode == 1 && kc * 32 + kic > rib[nt]) x = -INFINITY;
-      if (mode == 2 && kc * 32 + kic >= nvalid) x = -INFINITY;
-      const float p = __builtin_amdgcn_exp2f(x);
-      sum += p;
-      pk[r >> 3][r & 7] = (__bf16)p;
-    }
-    lsum[nt] += sum;
-  };
   auto pv = [&](const bf16x8 (&vop)[C::MT][2], const bf16x8 (&pk)[2], int nt) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
@@ -497,7 +475,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   // (fma, exp2, add; every second score the bf16 pair convert), so that each
   // gap between MFMAs holds a few VALU ops that issue under the MFMA in
   // flight.  Scores are tied to slots statically, whether or not the slot's
-  // MFMA exists in this stage.
+  // MFMA exists in this stage.  mode 0: plain; 1: diagonal block (causal
+  // mask); 2: pseudo-keys (slots >= nvalid masked).  Key-in-chunk of
+  // accumulator register r: 8*(r/4) + 4*hh + r%4.
   auto stage_mix = [&](const f32x16& Sin, int nts, int kc, int mode, int nvalid, float bias, bf16x8 (&pk)[2],
                        bool pv_on, const bf16x8 (&vv)[C::MT][2], const bf16x8 (&pp)[2], int ntp, bool qk_on,
                        const bf16x8 (&kk)[C::KS], const bf16x8 (&qs)[C::KS], f32x16& Sout)
