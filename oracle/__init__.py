@@ -44,4 +44,4 @@ from .attention import (  # noqa: F401
     kept_lists,
     score_band_mask,
 )
-from .e4m3 import e4m3_decode, dequantize  # noqa: F401
+from .e4m3 import e4m3_decode, e4m3_encode, dequantize  # noqa: F401

@@ -44,6 +44,41 @@ def test_e4m3_format_landmarks():
     assert np.signbit(dec(np.uint8(0x80))) and dec(np.uint8(0x80)) == 0.0
 
 
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    back = oracle.e4m3_encode(vals)
+    # -0 encodes as +0 (both decode to zero); every other code comes back
+    nz = vals != 0
+    assert np.array_equal(back[nz], codes[nz])
+    assert np.all(oracle.e4m3_decode(back[~nz]) == 0)
+
+
+def test_e4m3_encode_ties_saturation_nan():
+    enc, dec = oracle.e4m3_encode, oracle.e4m3_decode
+    # 1.0 (0x38) and 1.125 (0x39): the midpoint 1.0625 goes to the even code
+    assert enc(1.0625) == 0x38
+    # 1.125 (0x39) and 1.25 (0x3A): midpoint 1.1875 goes to 0x3A
+    assert enc(1.1875) == 0x3A
+    assert enc(1.0624) == 0x38 and enc(1.0626) == 0x39
+    # subnormal tie: 2^-10 lies midway between 0 and 2^-9 -> 0
+    assert enc(2.0 ** -10) == 0x00 and enc(1.5 * 2.0 ** -9) == 0x02
+    assert enc(448.0) == 0x7E and enc(1e9) == 0x7E and enc(-1e9) == 0xFE
+    assert enc(464.0) == 0x7E            # beyond 448: saturates, no infinity
+    assert enc(np.nan) == 0x7F
+    assert dec(enc(-3.3)) == -3.25
+
+
+def test_e4m3_encode_matches_torch_cast():
+    x = _rand(20000, scale=40.0)
+    x = np.concatenate([x, _rand(2000, scale=0.01)])
+    ours = oracle.e4m3_encode(x)
+    # torch's cast (RNE); its saturation is applied by clamping first
+    ref = torch.from_numpy(np.clip(x, -448.0, 448.0)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    zero = (oracle.e4m3_decode(ours) == 0) & (oracle.e4m3_decode(ref) == 0)
+    assert np.all(zero | (ours == ref))
+
+
 def test_dequantize_per_head_axis():
     codes = np.array([[0x38, 0x40], [0x38, 0x40]], dtype=np.uint8)  # 1.0, 2.0
     out = oracle.dequantize(codes, np.array([3.0, 5.0]), head_axis=1)
