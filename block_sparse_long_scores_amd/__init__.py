@@ -43,6 +43,7 @@ class Fp2Params(ctypes.Structure):
         ("q_scale", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
+        ("o_scale", ctypes.c_void_p),
     ]
 
 
@@ -171,9 +172,11 @@ def fp2_version():
 # ------------------------------------------------------------------ torch helpers
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"), softmax_scale=0.0,
-                mean_correction=True, fp8=False, out_fp32=False, q_scale=None, k_scale=None, v_scale=None):
-    """Build an ``Fp2Params``; fp8 scales are device fp32 tensors.  The params
-    object holds references to them, so they live as long as it does."""
+                mean_correction=True, fp8=False, out_fp32=False, q_scale=None, k_scale=None, v_scale=None,
+                out_fp8=False, o_scale=None):
+    """Build an ``Fp2Params``; fp8 scales are device fp32 tensors (o_scale: one
+    element, for out_fp8: e4m3 output codes, value = code * o_scale).  The
+    params object holds references to them, so they live as long as it does."""
     p = Fp2Params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -183,11 +186,12 @@ def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"
     p.tau = tau
     p.mean_correction = 1 if mean_correction else 0
     p.in_dtype = FP2_FP8_E4M3 if fp8 else FP2_BF16
-    p.out_dtype = FP2_FP32 if out_fp32 else FP2_BF16
+    p.out_dtype = FP2_FP8_E4M3 if out_fp8 else FP2_FP32 if out_fp32 else FP2_BF16
     p.q_scale = q_scale.data_ptr() if q_scale is not None else None
     p.k_scale = k_scale.data_ptr() if k_scale is not None else None
     p.v_scale = v_scale.data_ptr() if v_scale is not None else None
-    p._scale_tensors = (q_scale, k_scale, v_scale)
+    p.o_scale = o_scale.data_ptr() if o_scale is not None else None
+    p._scale_tensors = (q_scale, k_scale, v_scale, o_scale)
     return p
 
 
@@ -231,7 +235,7 @@ def select_blocks(params, q, k, v, workspace=None):
 
 
 def _out_like(params, q):
-    dt = torch.float32 if params.out_dtype == FP2_FP32 else torch.bfloat16
+    dt = {FP2_FP32: torch.float32, FP2_FP8_E4M3: torch.uint8}.get(params.out_dtype, torch.bfloat16)
     return torch.empty(q.shape, dtype=dt, device=q.device)
 
 

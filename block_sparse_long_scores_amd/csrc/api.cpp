@@ -71,8 +71,10 @@ fp2_status check_params(const fp2_params* p) {
     return fail(FP2_EINVAL, "softmax_scale is not finite");
   if (p->in_dtype != FP2_BF16 && p->in_dtype != FP2_FP8_E4M3)
     return fail(FP2_EUNSUPPORTED, "in_dtype=%d not supported", p->in_dtype);
-  if (p->out_dtype != FP2_BF16 && p->out_dtype != FP2_FP32)
+  if (p->out_dtype != FP2_BF16 && p->out_dtype != FP2_FP32 && p->out_dtype != FP2_FP8_E4M3)
     return fail(FP2_EUNSUPPORTED, "out_dtype=%d not supported", p->out_dtype);
+  if (p->out_dtype == FP2_FP8_E4M3 && !p->o_scale)
+    return fail(FP2_EINVAL, "out_dtype FP8_E4M3 needs o_scale");
   if (p->in_dtype == FP2_FP8_E4M3 && (!p->q_scale || !p->k_scale || !p->v_scale))
     return fail(FP2_EINVAL, "fp8 inputs need q_scale, k_scale and v_scale");
   if (p->mean_correction != 0 && p->mean_correction != 1)
@@ -107,7 +109,8 @@ void fill_attn_common(AttnArgs& a, const fp2_params* p) {
   a.Hkv = p->num_kv_heads;
   a.G = p->num_q_heads / p->num_kv_heads;
   a.scale_log2 = scale_of(p) * 1.4426950408889634f;
-  a.out_fp32 = p->out_dtype == FP2_FP32;
+  a.out_mode = p->out_dtype == FP2_FP32 ? 1 : p->out_dtype == FP2_FP8_E4M3 ? 2 : 0;
+  a.o_scale = p->out_dtype == FP2_FP8_E4M3 ? p->o_scale : nullptr;
   a.q_scale = p->q_scale;
   a.k_scale = p->k_scale;
   a.v_scale = p->v_scale;

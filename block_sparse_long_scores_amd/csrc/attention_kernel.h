@@ -962,8 +962,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   }
 
   // ---- epilogue: O = O^T / l (fp8: times the head's v scale), LSE
-  const bool out32 = a.out_fp32;
-  const float oscale = F8 ? a.v_scale[h] : 1.f;
+  // output: fp32, bf16, or e4m3 codes of out / o_scale (RNE, saturated)
+  const int omode = a.out_mode;
+  const float oscale = (F8 ? a.v_scale[h] : 1.f) * (omode == 2 ? 1.f / *a.o_scale : 1.f);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     int rb;
@@ -979,7 +980,20 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
                                            : ((long)s * a.Hq + h * G + gq) * a.lse_stride + r;
         a.lse[li] = (mref[nt] + log2f(lt)) * kLn2;
       }
-      if (out32) {
+      if (omode == 2) {
+        unsigned char* dst = (unsigned char*)a.out + off + 4 * hh;
+#pragma unroll
+        for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(O[mt][nt][4 * q4 + e] * inv, -448.f), 448.f);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+            *(int*)(dst + 32 * mt + 8 * q4) = w;
+          }
+      } else if (omode == 1) {
         float* dst = (float*)a.out + off + 4 * hh;
 #pragma unroll
         for (int mt = 0; mt < C::MT; ++mt)

@@ -81,7 +81,8 @@ struct AttnArgs {
   float scale_log2;         // softmax_scale * log2(e)
   int sparse;               // 1: block list + optional correction; 0: dense
   int mean_correction;
-  int out_fp32;
+  int out_mode;             // output dtype: 0 bf16, 1 fp32, 2 e4m3 (codes of out / *o_scale)
+  const float* o_scale;     // e4m3 output: per-tensor scale (device)
   int parts;                // workgroups per (seq, head, q-block) tile
   int waves;                // waves per workgroup
   int nqb_grid;             // query-block extent of the tile space

@@ -45,7 +45,7 @@
  *    returns FP2_EDEVICE.  No C++ exception crosses this interface.
  *  - Supported shapes: head_dim in {64, 128}; block_size in {64, 128};
  *    num_q_heads a positive multiple of num_kv_heads; in_dtype FP2_BF16 or
- *    FP2_FP8_E4M3; out_dtype FP2_BF16 or FP2_FP32.
+ *    FP2_FP8_E4M3; out_dtype FP2_BF16, FP2_FP32 or FP2_FP8_E4M3 (with o_scale).
  */
 #ifndef FP2_H
 #define FP2_H
@@ -76,13 +76,18 @@ typedef struct {
   float tau;               /* threshold; +INFINITY keeps every block; NaN is an error */
   int32_t mean_correction; /* 0: drop blocks outright; 1: pseudo-key correction */
   int32_t in_dtype;        /* fp2_dtype of q, k, v: FP2_BF16 or FP2_FP8_E4M3   */
-  int32_t out_dtype;       /* fp2_dtype of out: FP2_BF16 or FP2_FP32           */
+  int32_t out_dtype;       /* fp2_dtype of out: FP2_BF16, FP2_FP32 or FP2_FP8_E4M3 */
   /* FP8 only (E4M3, OCP "e4m3fn" encoding): per-head dequantization scales,
    * DEVICE fp32 arrays q_scale [Hq], k_scale [Hkv], v_scale [Hkv]; a value is
    * code * scale.  Ignored for bf16 inputs.                                   */
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
+  /* FP8 output only (out_dtype FP2_FP8_E4M3, any in_dtype): DEVICE pointer to
+   * one fp32 per-tensor scale; the output value is code * (*o_scale).  Codes
+   * are round-to-nearest-even of out / o_scale, saturated to +-448 (e4m3fn
+   * has no infinity).  Must be a positive finite value; ignored otherwise.  */
+  const float* o_scale;
 } fp2_params;
 
 /* Number of query blocks a sequence touches: blocks of absolute positions

@@ -80,6 +80,10 @@ def test_validation_errors():
     p.out_dtype = 7
     assert fp2.fp2_dense_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == fp2.FP2_EUNSUPPORTED
     p = params()
+    p.out_dtype = fp2.FP2_FP8_E4M3                          # e4m3 output without its scale
+    assert fp2.fp2_dense_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == fp2.FP2_EINVAL
+    assert "o_scale" in fp2.last_error()
+    p = params()
     p.mean_correction = 1
     assert fp2.fp2_sparse_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
                                   None) == fp2.FP2_EINVAL   # correction needs pooled blocks

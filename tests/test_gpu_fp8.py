@@ -198,3 +198,71 @@ def test_fp8_paged_matches_oracle_and_contiguous(gpu, page):
         torch.cuda.synchronize()
         assert torch.equal(c2[0], cnt[s, :, :geo.nqb])
         assert torch.equal(o2, out[cu[s]:cu[s + 1]])
+
+
+def _code_steps(a, b):
+    """Distance in e4m3 code steps between two uint8 code arrays (signed
+    magnitude order; +0 and -0 are the same point)."""
+    def ordinal(c):
+        c = c.astype(np.int64)
+        mag = c & 0x7F
+        return np.where(c & 0x80, -mag, mag)
+    return np.abs(ordinal(a) - ordinal(b))
+
+
+@pytest.mark.parametrize("fp8_in,headroom", [(False, 1.25), (True, 1.25), (False, 0.5)])
+def test_e4m3_output_codes(gpu, fp8_in, headroom):
+    """e4m3 output (value = code * o_scale, RNE, saturated at 448) against
+    the oracle's output encoded with the same scale, and against the same
+    call's fp32 output encoded on the host.  headroom < 1 puts the largest
+    outputs beyond 448 * o_scale (saturation)."""
+    S, hq, hkv, d, b = 1536, 8, 2, 128, 128
+    tau = 1.2
+    if fp8_in:
+        c = Fp8Case("planted", 21, S, hq, hkv, d, b)
+        q, k, v = c.q, c.k, c.v
+        qd, kd, vd = c.dev[:3]
+        mk = lambda **kw: c.params(gpu, tau, **kw)  # noqa: E731
+    else:
+        print(f"[case] bf16 in, e4m3 out S={S} headroom={headroom}", flush=True)
+        pr = synth.make_problem("planted", 21, S, hq, hkv, d, b)
+        q, k, v = (t.double().numpy() for t in (pr.q, pr.k, pr.v))
+        qd, kd, vd = pr.q.cuda(), pr.k.cuda(), pr.v.cuda()
+        mk = lambda **kw: gpu.make_params(hq, hkv, d, b, tau=tau, **kw)  # noqa: E731
+    p32 = mk(out_fp32=True)
+    idx, cnt, pk, pv = gpu.select_blocks(p32, qd, kd, vd)
+    out32 = gpu.sparse_prefill(p32, qd, kd, vd, idx, cnt, pk, pv)
+    torch.cuda.synchronize()
+    ref = A.sparse_prefill(q, k, v, hkv, b, tau, q_blocks=[])
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    O, _ = A.attend(q, k, v, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+    o_scale = float(np.abs(O).max()) / 448.0 * headroom
+    os_dev = torch.tensor([o_scale], dtype=torch.float32, device="cuda")
+    p8 = mk(out_fp8=True, o_scale=os_dev)
+    codes = gpu.sparse_prefill(p8, qd, kd, vd, idx, cnt, pk, pv)
+    torch.cuda.synchronize()
+    assert codes.dtype == torch.uint8
+    g = codes.cpu().numpy().reshape(O.shape)
+    want = oracle.e4m3_encode(O / np.float64(np.float32(o_scale)))
+    own = oracle.e4m3_encode(out32.double().cpu().numpy().reshape(O.shape) / np.float64(np.float32(o_scale)))
+    st_ref, st_own = _code_steps(g, want), _code_steps(g, own)
+    sat = float((np.abs(O) / o_scale > 448).mean())
+    # decoded against the oracle's float64 output (values beyond the range
+    # compare with their saturated value): e4m3 rounding (half a step, at
+    # most 2^-4 relative, 2^-10 o_scale absolute in the subnormals) on top of
+    # the attention path's own tolerance
+    dec = oracle.e4m3_decode(g) * np.float64(np.float32(o_scale))
+    Oc = np.clip(O, -448 * o_scale, 448 * o_scale)
+    err = np.abs(dec - Oc)
+    att_tol = FP8_REL_L2 if fp8_in else 2e-2
+    bound = 2.0 ** -4 * np.abs(Oc) + 2.0 ** -10 * o_scale + att_tol * np.abs(Oc).max()
+    e = rel_l2(dec, Oc)
+    print(f"[e4m3 out fp8_in={fp8_in} headroom={headroom}] saturated={sat:.4f} rel_l2 vs oracle {e:.3e}, codes "
+          f"equal to the oracle's {(st_ref == 0).mean():.4f}, to the encoded fp32 output {(st_own == 0).mean():.5f} "
+          f"(max {st_own.max()} step)", flush=True)
+    assert not np.any((g & 0x7F) == 0x7F), "an e4m3 NaN code was written"
+    assert np.all(err <= bound) and e < FP8_REL_L2
+    assert st_own.max() <= 1 and (st_own == 0).mean() > 0.999
+    if headroom < 1:
+        assert sat > 0 and np.all((g[np.abs(O) / o_scale > 449] & 0x7F) == 0x7E)

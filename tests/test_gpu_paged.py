@@ -54,3 +54,37 @@ def test_paged_matches_oracle_and_contiguous(gpu, d, b, page):
         torch.cuda.synchronize()
         assert torch.equal(c2[0], cnt[s, :, :geo.nqb])
         assert torch.equal(o2, out[cu[s]:cu[s + 1]])
+
+
+def test_paged_mixed_prefill_and_decode_rows(gpu):
+    """One call mixing decode rows (a one-row new chunk after a cached prefix),
+    a chunked prefill and a full prefill, as continuous batching issues them:
+    a decode row is a query block of one row, selected and attended like any
+    other.  Positions cover a decode row that opens a new key block (kv_len
+    = 1025: its diagonal block holds the one new key) and one deep in a block."""
+    hq, hkv, d, b, page = 8, 2, 128, 128, 64
+    kv_lens = [1500, 1025, 2048, 300, 4000]
+    q_lens = [1, 1, 700, 300, 1]
+    print(f"[case] mixed decode kv_lens={kv_lens} q_lens={q_lens}", flush=True)
+    pb = synth.make_paged(13, kv_lens, q_lens, hq, hkv, d, b, page_size=page)
+    tau = 0.8
+    p = gpu.make_params(hq, hkv, d, b, tau=tau)
+    out, (idx, cnt), lse = gpu.sparse_prefill_paged(
+        p, pb.q.cuda(), pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda(), max(q_lens), max(kv_lens), pb.k_cache.cuda(),
+        pb.v_cache.cuda(), pb.page_table.cuda(), export_mask=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "a canary (NaN) page was read"
+    cu = pb.cu_seqlens_q.numpy()
+    for s, seq in enumerate(pb.seqs):
+        qn, kn, vn = f64(seq["q"]), f64(seq["k"]), f64(seq["v"])
+        ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, q_blocks=[])
+        geo = ref["geo"]
+        kept_gpu = kept_from_lists(idx[s, :, :geo.nqb], cnt[s, :, :geo.nqb], geo.nkb)
+        assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
+        O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+        o = f64(out[cu[s]:cu[s + 1]])
+        e, m = rel_l2(o, O), max_abs(o, O)
+        print(f"[mixed] seq {s}: q_len={q_lens[s]} nqb={geo.nqb} kept={int(kept_gpu.sum())} rel_l2={e:.2e} "
+              f"max_abs={m:.2e}", flush=True)
+        assert e < BF16_REL_L2 and m < BF16_MAX_ABS
+        assert np.abs(f64(lse[cu[s]:cu[s + 1]]).T - L).max() < 2e-2
