@@ -71,6 +71,9 @@ _SIGS = {
     "fp2_paged_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "fp2_sparse_prefill_paged": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp,
                                                 _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fp2_sparse_prefill_paged_pooled": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
+                                                       _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp,
+                                                       _vp]),
     "fp2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp2_last_error": (ctypes.c_char_p, []),
     "fp2_version": (ctypes.c_char_p, []),
@@ -155,6 +158,17 @@ def fp2_sparse_prefill_paged(params, num_seqs, q, cu_seqlens_q, seqlens_k, max_s
                                            max_seqlen_k, k_cache, v_cache, num_pages, page_size, page_table,
                                            max_pages_per_seq, out, lse, block_idx, block_cnt, workspace,
                                            workspace_bytes, stream)
+
+
+def fp2_sparse_prefill_paged_pooled(params, num_seqs, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k,
+                                    k_cache, v_cache, num_pages, page_size, page_table, max_pages_per_seq, out, lse,
+                                    block_idx, block_cnt, workspace, workspace_bytes, block_sums_k, block_sums_v,
+                                    cached_blocks, stream):
+    return load().fp2_sparse_prefill_paged_pooled(ctypes.byref(params), num_seqs, q, cu_seqlens_q, seqlens_k,
+                                                  max_seqlen_q, max_seqlen_k, k_cache, v_cache, num_pages, page_size,
+                                                  page_table, max_pages_per_seq, out, lse, block_idx, block_cnt,
+                                                  workspace, workspace_bytes, block_sums_k, block_sums_v,
+                                                  cached_blocks, stream)
 
 
 def fp2_status_string(status):
@@ -263,9 +277,19 @@ def dense_prefill(params, q, k, v, out=None, lse=None, return_lse=False):
     return (out, lse) if return_lse else out
 
 
+def block_sum_cache(params, k_cache):
+    """Zeroed key-block sum cache for ``sparse_prefill_paged(pool_cache=...)``:
+    (block_sums_k, block_sums_v) fp32 [num_pages, Hkv, d]."""
+    shape = (k_cache.shape[0], params.num_kv_heads, params.head_dim)
+    return (torch.zeros(shape, dtype=torch.float32, device=k_cache.device),
+            torch.zeros(shape, dtype=torch.float32, device=k_cache.device))
+
+
 def sparse_prefill_paged(params, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache,
-                         page_table, export_mask=False, return_lse=False, out=None, workspace=None):
+                         page_table, export_mask=False, return_lse=False, out=None, workspace=None, pool_cache=None):
     """Paged-KV continuous batch.  q [total_q,Hq,d]; caches [pages,page,Hkv,d].
+    pool_cache = (block_sums_k, block_sums_v, cached_blocks [n] int32): key-block
+    sums kept across calls (fp2_sparse_prefill_paged_pooled).
     Returns out (and (block_idx, block_cnt) if export_mask, lse if return_lse)."""
     n = seqlens_k.shape[0]
     dev = q.device
@@ -279,12 +303,22 @@ def sparse_prefill_paged(params, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_s
     ws_bytes = fp2_paged_workspace_size(params, n, max_seqlen_q, max_seqlen_k)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    st = fp2_sparse_prefill_paged(params, n, q.data_ptr(), cu_seqlens_q.data_ptr(), seqlens_k.data_ptr(),
-                                  max_seqlen_q, max_seqlen_k, k_cache.data_ptr(), v_cache.data_ptr(),
-                                  k_cache.shape[0], k_cache.shape[1], page_table.data_ptr(), page_table.shape[1],
-                                  out.data_ptr(), _ptr(lse), _ptr(idx), _ptr(cnt), workspace.data_ptr(),
-                                  workspace.numel(), _stream())
-    _check(st, "fp2_sparse_prefill_paged")
+    if pool_cache is None:
+        st = fp2_sparse_prefill_paged(params, n, q.data_ptr(), cu_seqlens_q.data_ptr(), seqlens_k.data_ptr(),
+                                      max_seqlen_q, max_seqlen_k, k_cache.data_ptr(), v_cache.data_ptr(),
+                                      k_cache.shape[0], k_cache.shape[1], page_table.data_ptr(), page_table.shape[1],
+                                      out.data_ptr(), _ptr(lse), _ptr(idx), _ptr(cnt), workspace.data_ptr(),
+                                      workspace.numel(), _stream())
+        _check(st, "fp2_sparse_prefill_paged")
+    else:
+        bsk, bsv, cached = pool_cache
+        st = fp2_sparse_prefill_paged_pooled(params, n, q.data_ptr(), cu_seqlens_q.data_ptr(), seqlens_k.data_ptr(),
+                                             max_seqlen_q, max_seqlen_k, k_cache.data_ptr(), v_cache.data_ptr(),
+                                             k_cache.shape[0], k_cache.shape[1], page_table.data_ptr(),
+                                             page_table.shape[1], out.data_ptr(), _ptr(lse), _ptr(idx), _ptr(cnt),
+                                             workspace.data_ptr(), workspace.numel(), bsk.data_ptr(), _ptr(bsv),
+                                             cached.data_ptr(), _stream())
+        _check(st, "fp2_sparse_prefill_paged_pooled")
     res = [out]
     if export_mask:
         res.append((idx, cnt))

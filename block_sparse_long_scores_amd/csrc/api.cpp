@@ -295,12 +295,12 @@ size_t fp2_paged_workspace_size(const fp2_params* p, int32_t num_seqs, int32_t m
   return paged_layout(p, num_seqs, nq, nk).total;
 }
 
-fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const void* q, const int32_t* cu_seqlens_q,
-                                    const int32_t* seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                    const void* k_cache, const void* v_cache, int32_t num_pages, int32_t page_size,
-                                    const int32_t* page_table, int32_t max_pages_per_seq, void* out, float* lse,
-                                    int32_t* block_idx, int32_t* block_cnt, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* q, const int32_t* cu_seqlens_q,
+                             const int32_t* seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             const void* k_cache, const void* v_cache, int32_t num_pages, int32_t page_size,
+                             const int32_t* page_table, int32_t max_pages_per_seq, void* out, float* lse,
+                             int32_t* block_idx, int32_t* block_cnt, void* workspace, size_t workspace_bytes,
+                             void* stream, float* bsum_k, float* bsum_v, const int32_t* cached_blocks) {
   fp2_status st = check_params(p);
   if (st != FP2_OK) return st;
   if ((st = check_lengths(num_seqs, max_seqlen_q, max_seqlen_k)) != FP2_OK) return st;
@@ -374,6 +374,9 @@ fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const
   pa.D = D;
   pa.block = b;
   pa.fp8 = p->in_dtype == FP2_FP8_E4M3;
+  pa.bsum_k = bsum_k;
+  pa.bsum_v = bsum_v;
+  pa.cached_blocks = cached_blocks;
   hipError_t e = launch_pool(pa, s);
   if (e != hipSuccess) return device_status(e, "pool kernel launch");
   SelectArgs sa{};
@@ -422,6 +425,34 @@ fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const
     fprintf(stderr, "[fp2] paged n=%d max_sq=%d max_sk=%d page=%d max_nqb=%d max_nkb=%d\n", num_seqs, max_seqlen_q,
             max_seqlen_k, page_size, max_nqb, max_nkb);
   return ok();
+}
+
+fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const void* q, const int32_t* cu_seqlens_q,
+                                    const int32_t* seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    const void* k_cache, const void* v_cache, int32_t num_pages, int32_t page_size,
+                                    const int32_t* page_table, int32_t max_pages_per_seq, void* out, float* lse,
+                                    int32_t* block_idx, int32_t* block_cnt, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return paged_impl(p, num_seqs, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache, num_pages,
+                    page_size, page_table, max_pages_per_seq, out, lse, block_idx, block_cnt, workspace,
+                    workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+fp2_status fp2_sparse_prefill_paged_pooled(const fp2_params* p, int32_t num_seqs, const void* q,
+                                           const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                           int32_t max_seqlen_q, int32_t max_seqlen_k, const void* k_cache,
+                                           const void* v_cache, int32_t num_pages, int32_t page_size,
+                                           const int32_t* page_table, int32_t max_pages_per_seq, void* out,
+                                           float* lse, int32_t* block_idx, int32_t* block_cnt, void* workspace,
+                                           size_t workspace_bytes, float* block_sums_k, float* block_sums_v,
+                                           const int32_t* cached_blocks, void* stream) {
+  if (!p) return fail(FP2_EINVAL, "params is NULL");
+  if (!block_sums_k || !cached_blocks || (p->mean_correction && !block_sums_v))
+    return fail(FP2_EINVAL, "block_sums_k, cached_blocks (and block_sums_v with mean correction) must be non-NULL");
+  return paged_impl(p, num_seqs, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache, v_cache, num_pages,
+                    page_size, page_table, max_pages_per_seq, out, lse, block_idx, block_cnt, workspace,
+                    workspace_bytes, stream, block_sums_k, p->mean_correction ? block_sums_v : nullptr,
+                    cached_blocks);
 }
 
 const char* fp2_status_string(fp2_status s) {

@@ -41,6 +41,13 @@ struct PoolArgs {
   const float* k_scale;
   const float* v_scale;
   int Hq, Hkv, D, block, fp8;
+  // Paged calls with a block-sum cache (or nullptr): fp32 row sums of full
+  // key blocks, [num_pages, Hkv * D] each, at the physical id of the block's
+  // first page; blocks below cached_blocks[s] are read from it, every other
+  // full block is summed and written to it.
+  float* bsum_k;
+  float* bsum_v;
+  const int* cached_blocks;
 };
 
 struct SelectArgs {

@@ -132,7 +132,31 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   for (int c = 0; c < kMaxChunksPerThread; ++c)
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
-  for (int cc = c0; cc < c1; ++cc) {
+  // block-sum cache (paged): the entry of a full block sits at the physical
+  // id of its first page and holds the same fp32 sums, in the same order, as
+  // the row loop below
+  float* csk = nullptr;
+  float* csv = nullptr;
+  bool from_cache = false;
+  if (a.bsum_k && c1 - c0 == a.block) {
+    const long pg = a.kv.page_table[(long)s * a.kv.max_pages + (c0 >> a.kv.page_log2)];
+    csk = a.bsum_k + pg * W;
+    csv = a.bsum_v ? a.bsum_v + pg * W : nullptr;
+    from_cache = j < a.cached_blocks[s];
+  }
+  if (from_cache) {
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      const int task = t + c * kPoolThreads;
+      if (task < ntask) {
+        const bool isv = task >= nch;
+        const float* src = (isv ? csv : csk) + (isv ? task - nch : task) * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[c][e] = src[e];
+      }
+    }
+  }
+  for (int cc = from_cache ? c1 : c0; cc < c1; ++cc) {
     const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc, rowbytes);
     const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc, rowbytes);
     uint4 w[kMaxChunksPerThread];
@@ -148,6 +172,18 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
 #pragma unroll
     for (int c = 0; c < kMaxChunksPerThread; ++c)
       if (t + c * kPoolThreads < ntask) acc_chunk<ESZ>(acc[c], w[c]);
+  }
+  if (csk && !from_cache) {
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      const int task = t + c * kPoolThreads;
+      if (task < ntask) {
+        const bool isv = task >= nch;
+        float* dst = (isv ? csv : csk) + (isv ? task - nch : task) * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) dst[e] = acc[c][e];
+      }
+    }
   }
   const float inv = 1.f / (float)(c1 - c0);
 #pragma unroll

@@ -186,6 +186,38 @@ fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* fp2_sparse_prefill_paged with a caller-kept cache of key-block sums, for
+ * chunked prefill ([EXP] §2.3: paged KV with chunked prefill; the pooled
+ * statistics of a cached prefix do not change between its chunks, so they
+ * are kept next to the KV cache instead of re-read from it every chunk).
+ *   block_sums_k, block_sums_v : fp32 [num_pages, Hkv, d] (DEVICE, caller
+ *       owned, kept across calls).  The entry of a FULL key block (block_size
+ *       keys) of a sequence sits at the physical id of the block's first page
+ *       and holds the fp32 row sums of its K (and V) rows, in code units for
+ *       fp8 inputs.  block_sums_v may be NULL when mean_correction is 0.
+ *   cached_blocks : int32 [num_seqs] (DEVICE): key blocks [0, cached_blocks[s])
+ *       of sequence s are read from the cache (they must be full and unchanged
+ *       since they were written); every other full block of the call is summed
+ *       from the pages and written to the cache.  After the call, the full
+ *       blocks of sequence s are its first seqlens_k[s] / block_size blocks,
+ *       which is what cached_blocks[s] may be set to for its next chunk.  A
+ *       page freed or rewritten invalidates the entry of the block it starts.
+ * Results are bit-identical to fp2_sparse_prefill_paged on the same inputs
+ * (the cached sums are the same fp32 sums in the same order).  Errors as
+ * fp2_sparse_prefill_paged, plus FP2_EINVAL for a NULL cache argument.        */
+fp2_status fp2_sparse_prefill_paged_pooled(const fp2_params* p, int32_t num_seqs,
+                                           const void* q, const int32_t* cu_seqlens_q,
+                                           const int32_t* seqlens_k,
+                                           int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                           const void* k_cache, const void* v_cache,
+                                           int32_t num_pages, int32_t page_size,
+                                           const int32_t* page_table, int32_t max_pages_per_seq,
+                                           void* out, float* lse,
+                                           int32_t* block_idx, int32_t* block_cnt,
+                                           void* workspace, size_t workspace_bytes,
+                                           float* block_sums_k, float* block_sums_v,
+                                           const int32_t* cached_blocks, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* fp2_status_string(fp2_status s);
 /* Description of the last error raised on the calling thread ("" if none). */

@@ -109,6 +109,17 @@ def test_paged_validation_errors():
     assert call(wsb=1024) == fp2.FP2_EWORKSPACE
     assert call(npages=0) == fp2.FP2_EINVAL
 
+    def pooled(bsk=FAKE, bsv=FAKE, cached=FAKE, **kw):
+        a = dict(args)
+        a.update(kw)
+        return fp2.fp2_sparse_prefill_paged_pooled(p, 2, a["q"], a["cu"], a["sk"], a["mq"], a["mk"], a["kc"], a["vc"],
+                                                   a["npages"], a["page"], a["table"], a["mpp"], a["out"], a["lse"],
+                                                   a["idx"], a["cnt"], a["ws"], a["wsb"], bsk, bsv, cached, None)
+    assert pooled(bsk=None) == fp2.FP2_EINVAL
+    assert pooled(cached=None) == fp2.FP2_EINVAL
+    assert pooled(bsv=None) == fp2.FP2_EINVAL               # mean correction needs the V sums
+    assert pooled(page=48) == fp2.FP2_EUNSUPPORTED          # the paged checks apply as well
+
 
 def test_status_strings():
     assert fp2.status_string(fp2.FP2_OK) == "FP2_OK"

@@ -88,3 +88,64 @@ def test_paged_mixed_prefill_and_decode_rows(gpu):
               f"max_abs={m:.2e}", flush=True)
         assert e < BF16_REL_L2 and m < BF16_MAX_ABS
         assert np.abs(f64(lse[cu[s]:cu[s + 1]]).T - L).max() < 2e-2
+
+
+def _same_masks(m1, m2, lo, hi, b):
+    """Exported masks of two calls agree on every defined entry (each
+    sequence's query blocks; the lists up to their counts)."""
+    for s in range(len(hi)):
+        geo = A.geometry(hi[s] - lo[s], hi[s], b)
+        c1, c2 = m1[1][s, :, :geo.nqb], m2[1][s, :, :geo.nqb]
+        assert torch.equal(c1, c2), s
+        k1 = kept_from_lists(m1[0][s, :, :geo.nqb], c1, geo.nkb)
+        k2 = kept_from_lists(m2[0][s, :, :geo.nqb], c2, geo.nkb)
+        assert np.array_equal(k1, k2), s
+
+
+def test_paged_block_sum_cache_chunked_prefill(gpu):
+    """Chunked prefill with the key-block sum cache (fp2_sparse_prefill_paged_
+    pooled): each chunk's call reads the sums of the full blocks its earlier
+    chunks wrote and must give bit-identical masks, outputs and LSE to the
+    uncached call; the cache entries must be the row sums of the blocks."""
+    hq, hkv, d, b, page = 8, 2, 128, 128, 64
+    L = [2048, 1500]
+    bounds = [[0, 700, 1300, 2048], [0, 500, 1000, 1500]]   # chunk ends, not block aligned
+    print(f"[case] block-sum cache L={L} chunks={bounds}", flush=True)
+    pb = synth.make_paged(14, L, L, hq, hkv, d, b, page_size=page)
+    tau = 0.8
+    p = gpu.make_params(hq, hkv, d, b, tau=tau)
+    kc, vc, tab = pb.k_cache.cuda(), pb.v_cache.cuda(), pb.page_table.cuda()
+    bsk, bsv = gpu.block_sum_cache(p, kc)
+    cached = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for c in range(3):
+        lo = [bounds[s][c] for s in range(2)]
+        hi = [bounds[s][c + 1] for s in range(2)]
+        q = torch.cat([pb.seqs[s]["q"][lo[s]:hi[s]] for s in range(2)], 0).cuda()
+        cu = torch.tensor([0, hi[0] - lo[0], hi[0] - lo[0] + hi[1] - lo[1]], dtype=torch.int32, device="cuda")
+        sk = torch.tensor(hi, dtype=torch.int32, device="cuda")
+        args = (p, q, cu, sk, max(h - l for h, l in zip(hi, lo)), max(hi), kc, vc, tab)
+        o1, m1, l1 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True)
+        o2, m2, l2 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True, pool_cache=(bsk, bsv, cached))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"chunk {c}"
+        _same_masks(m1, m2, lo, hi, b)
+        cached = (sk // b).to(torch.int32)
+        # the cache now holds every full block of the prefix: compare with the oracle's block sums
+        for s in range(2):
+            k = f64(pb.seqs[s]["k"][:hi[s]])
+            v = f64(pb.seqs[s]["v"][:hi[s]])
+            for j in range(hi[s] // b):
+                pg = int(pb.page_table[s, (j * b) // page])
+                ksum = k[j * b:(j + 1) * b].sum(0)          # [Hkv, d]
+                vsum = v[j * b:(j + 1) * b].sum(0)
+                gk = bsk[pg].double().cpu().numpy()
+                gv = bsv[pg].double().cpu().numpy()
+                assert np.abs(gk - ksum).max() <= 1e-5 * np.abs(ksum).max() + 1e-4, (c, s, j)
+                assert np.abs(gv - vsum).max() <= 1e-5 * np.abs(vsum).max() + 1e-4, (c, s, j)
+        print(f"[cache] chunk {c}: q rows {hi[0] - lo[0]}+{hi[1] - lo[1]}, cached blocks now {cached.tolist()}",
+              flush=True)
+    # a repeat of the last chunk reads every full block from the cache
+    o3, m3, l3 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True, pool_cache=(bsk, bsv, cached))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    _same_masks(m1, m3, lo, hi, b)
