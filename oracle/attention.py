@@ -125,6 +125,44 @@ def select(S, q_block_ids, tau):
     return kept, thr
 
 
+def pool_q_heads(q, seqlen_k, block):
+    """Per-query-head block means (selection variant "union"): qbar_heads
+    [Hq, nqb, d], each the mean over the rows of block i present in this call."""
+    Sq, Hq, d = q.shape
+    geo = geometry(Sq, seqlen_k, block)
+    out = np.empty((Hq, geo.nqb, d))
+    for il, i in enumerate(geo.q_block_ids()):
+        r0, r1 = geo.q_rows(i)
+        out[:, il, :] = _f64(q[r0:r1]).mean(axis=0)
+    return out
+
+
+def select_union(qbar_heads, kbar, q_block_ids, tau):
+    """Selection variant "union" (a reading for per-query-head masks under
+    GQA packing, whose K/V tile is shared by the group): every query head
+    applies the max-threshold rule to its own scores <qbar_hq, kbar_j>, and a
+    key block is kept for the group if any of its heads keeps it (plus the
+    sink and diagonal blocks).  Returns kept [Hkv, nqb, nkb], the per-head
+    scores S [Hq, nqb, nkb] and thresholds [Hq, nqb]."""
+    Hq = qbar_heads.shape[0]
+    Hkv = kbar.shape[0]
+    G = Hq // Hkv
+    kbar_heads = np.repeat(kbar, G, axis=0)          # query head hq reads group hq // G
+    S = block_scores(qbar_heads, kbar_heads, q_block_ids)
+    kept_heads, thr = select(S, q_block_ids, tau)
+    kept = kept_heads.reshape(Hkv, G, *kept_heads.shape[1:]).any(axis=1)
+    return kept, S, thr
+
+
+def union_band_mask(S_heads, thr_heads, num_kv_heads, band=1e-3):
+    """score_band_mask of the union selection: a group's block may differ
+    between two correct selections where any of its heads scores within
+    ``band`` of that head's threshold."""
+    b = score_band_mask(S_heads, thr_heads, band)
+    G = b.shape[0] // num_kv_heads
+    return b.reshape(num_kv_heads, G, *b.shape[1:]).any(axis=1)
+
+
 def kept_lists(kept):
     """Ascending kept-block list and count per (h, il), for comparison with a
     compacted index list."""
@@ -258,15 +296,22 @@ def dense_attention(q, k, v, num_kv_heads, scale, rows=None):
 
 
 def sparse_prefill(q, k, v, num_kv_heads, block, tau, scale=None,
-                   mean_correction=True, q_blocks=None):
-    """The whole pipeline on one sequence: pool, score, select, attend."""
+                   mean_correction=True, q_blocks=None, select_mode="mean"):
+    """The whole pipeline on one sequence: pool, score, select, attend.
+    select_mode "mean": one query mean per GQA group (the default reading);
+    "union": per-query-head selection, united over the group (S and thr are
+    then per query head)."""
     d = q.shape[2]
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
     geo = geometry(q.shape[0], k.shape[0], block)
     qbar, kbar, vbar, n_k = pool(q, k, v, num_kv_heads, block)
-    S = block_scores(qbar, kbar, geo.q_block_ids())
-    kept, thr = select(S, geo.q_block_ids(), tau)
+    if select_mode == "union":
+        qbar = pool_q_heads(q, k.shape[0], block)
+        kept, S, thr = select_union(qbar, kbar, geo.q_block_ids(), tau)
+    else:
+        S = block_scores(qbar, kbar, geo.q_block_ids())
+        kept, thr = select(S, geo.q_block_ids(), tau)
     O, LSE = attend(q, k, v, kept, kbar, vbar, n_k, num_kv_heads, block,
                     scale, mean_correction, q_blocks)
     return dict(geo=geo, qbar=qbar, kbar=kbar, vbar=vbar, n_k=n_k, S=S,

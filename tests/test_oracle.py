@@ -180,6 +180,77 @@ def test_select_invariants():
             assert set(np.flatnonzero(kept0[h, i])) == expect    # tau = 0
 
 
+def _brute_union(q, k, Hkv, b, tau):
+    """Per-query-head selection united over each group, with explicit loops:
+    head hq pools its own rows of each query block and applies the rule."""
+    Sq, Hq, d = q.shape
+    Sk = k.shape[0]
+    G = Hq // Hkv
+    P = Sk - Sq
+    first, last = P // b, (Sk - 1) // b
+    nkb = -(-Sk // b)
+    kept = np.zeros((Hkv, last - first + 1, nkb), dtype=bool)
+    for hq in range(Hq):
+        h = hq // G
+        for il, i in enumerate(range(first, last + 1)):
+            rows = [r for r in range(Sq) if (P + r) // b == i]
+            qm = [sum(q[r, hq, t] for r in rows) / len(rows) for t in range(d)]
+            s = []
+            for j in range(i + 1):
+                keys = [c for c in range(Sk) if c // b == j]
+                km = [sum(k[c, h, t] for c in keys) / len(keys) for t in range(d)]
+                s.append(sum(qm[t] * km[t] for t in range(d)))
+            m = max(s)
+            for j in range(i + 1):
+                if s[j] >= m - tau or j == 0 or j == i:
+                    kept[h, il, j] = True
+    return kept
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.4, 2.0])
+def test_select_union_matches_loops(tau):
+    Sq, Sk, Hq, Hkv, d, b = 21, 37, 6, 2, 3, 4
+    q, k = _rand(Sq, Hq, d), _rand(Sk, Hkv, d)
+    geo = A.geometry(Sq, Sk, b)
+    qh = A.pool_q_heads(q, Sk, b)
+    _, kbar, _, _ = A.pool(q, k, k, Hkv, b)
+    kept, S, thr = A.select_union(qh, kbar, geo.q_block_ids(), tau)
+    assert np.array_equal(kept, _brute_union(q, k, Hkv, b, tau))
+    assert S.shape == (Hq, geo.nqb, geo.nkb) and thr.shape == (Hq, geo.nqb)
+
+
+def test_select_union_reductions():
+    Sq = Sk = 48
+    Hkv, d, b = 2, 5, 8
+    k = _rand(Sk, Hkv, d)
+    ids = A.geometry(Sq, Sk, b).q_block_ids()
+    # one head per group: the union is the group-mean selection
+    q1 = _rand(Sq, Hkv, d)
+    _, kbar, _, _ = A.pool(q1, k, k, Hkv, b)
+    qbar, _, _, _ = A.pool(q1, k, k, Hkv, b)
+    for tau in [0.0, 0.5, 3.0]:
+        ku, _, _ = A.select_union(A.pool_q_heads(q1, Sk, b), kbar, ids, tau)
+        km, _ = A.select(A.block_scores(qbar, kbar, ids), ids, tau)
+        assert np.array_equal(ku, km)
+    # heads of a group with identical queries: the union is again the group-mean selection
+    G = 3
+    qg = np.repeat(_rand(Sq, Hkv, 1, d), G, axis=2).reshape(Sq, Hkv * G, d)
+    qbar, _, _, _ = A.pool(qg, k, k, Hkv, b)
+    for tau in [0.0, 0.5, 3.0]:
+        ku, _, _ = A.select_union(A.pool_q_heads(qg, Sk, b), kbar, ids, tau)
+        km, _ = A.select(A.block_scores(qbar, kbar, ids), ids, tau)
+        assert np.array_equal(ku, km)
+    # the union contains every head's own selection, the sink and the diagonal; tau = inf keeps all
+    q = _rand(Sq, Hkv * G, d)
+    qh = A.pool_q_heads(q, Sk, b)
+    ku, S, thr = A.select_union(qh, kbar, ids, 0.7)
+    kh, _ = A.select(S, ids, 0.7)
+    assert np.all(ku >= kh.reshape(Hkv, G, *kh.shape[1:]).any(axis=1))
+    assert ku[:, :, 0].all() and ku[:, np.arange(len(ids)), ids].all()
+    ki, _, _ = A.select_union(qh, kbar, ids, np.inf)
+    assert A.sparsity(ki, ids) == 0.0
+
+
 def test_sparsity_definition():
     kept = np.zeros((1, 4, 4), dtype=bool)
     kept[0, np.arange(4), np.arange(4)] = True    # 4 kept of 1+2+3+4 = 10 visible
