@@ -44,6 +44,7 @@ class Fp2Params(ctypes.Structure):
         ("k_scale", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p),
         ("o_scale", ctypes.c_void_p),
+        ("select_mode", ctypes.c_int32),
     ]
 
 
@@ -187,10 +188,12 @@ def fp2_version():
 
 def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"), softmax_scale=0.0,
                 mean_correction=True, fp8=False, out_fp32=False, q_scale=None, k_scale=None, v_scale=None,
-                out_fp8=False, o_scale=None):
+                out_fp8=False, o_scale=None, select_mode="mean"):
     """Build an ``Fp2Params``; fp8 scales are device fp32 tensors (o_scale: one
     element, for out_fp8: e4m3 output codes, value = code * o_scale).  The
-    params object holds references to them, so they live as long as it does."""
+    params object holds references to them, so they live as long as it does.
+    select_mode: "mean" (group-mean pooled query) or "union" (per query head,
+    united over the GQA group)."""
     p = Fp2Params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -205,6 +208,7 @@ def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"
     p.k_scale = k_scale.data_ptr() if k_scale is not None else None
     p.v_scale = v_scale.data_ptr() if v_scale is not None else None
     p.o_scale = o_scale.data_ptr() if o_scale is not None else None
+    p.select_mode = {"mean": 0, "union": 1}[select_mode]
     p._scale_tensors = (q_scale, k_scale, v_scale, o_scale)
     return p
 

@@ -79,6 +79,8 @@ fp2_status check_params(const fp2_params* p) {
     return fail(FP2_EINVAL, "fp8 inputs need q_scale, k_scale and v_scale");
   if (p->mean_correction != 0 && p->mean_correction != 1)
     return fail(FP2_EINVAL, "mean_correction=%d must be 0 or 1", p->mean_correction);
+  if (p->select_mode != 0 && p->select_mode != 1)
+    return fail(FP2_EINVAL, "select_mode=%d must be 0 or 1", p->select_mode);
   return FP2_OK;
 }
 
@@ -91,7 +93,7 @@ fp2_status check_lengths(int batch, int sq, int sk) {
 // Query blocks per select workgroup such that the score rows fit in LDS.
 int select_rows_per_wg(int D, int nkb) {
   for (int tq = 16; tq >= 1; tq >>= 1)
-    if ((size_t)tq * (D + nkb) * sizeof(float) <= 160 * 1024) return tq;
+    if ((size_t)tq * (D + nkb + (nkb + 31) / 32) * sizeof(float) <= 160 * 1024) return tq;
   return 0;
 }
 
@@ -139,7 +141,8 @@ int32_t fp2_num_k_blocks(int32_t seqlen_k, int32_t block_size) {
 size_t fp2_select_workspace_size(const fp2_params* p, int32_t batch, int32_t seqlen_q, int32_t seqlen_k) {
   if (check_params(p) != FP2_OK || check_lengths(batch, seqlen_q, seqlen_k) != FP2_OK) return 0;
   const int nqb = nq_blocks(seqlen_q, seqlen_k, p->block_size);
-  return align_up((size_t)batch * p->num_kv_heads * nqb * p->head_dim * sizeof(float));
+  const int qh = p->select_mode == 1 ? p->num_q_heads : p->num_kv_heads;  // pooled query rows per block
+  return align_up((size_t)batch * qh * nqb * p->head_dim * sizeof(float));
 }
 
 fp2_status fp2_select_blocks(const fp2_params* p, int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
@@ -176,6 +179,7 @@ fp2_status fp2_select_blocks(const fp2_params* p, int32_t batch, int32_t seqlen_
   pa.D = D;
   pa.block = b;
   pa.fp8 = p->in_dtype == FP2_FP8_E4M3;
+  pa.select_mode = p->select_mode;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_pool(pa, s);
   if (e != hipSuccess) return device_status(e, "pool kernel launch");
@@ -190,6 +194,8 @@ fp2_status fp2_select_blocks(const fp2_params* p, int32_t batch, int32_t seqlen_
   sa.block = b;
   sa.tau = p->tau;
   sa.rows_per_wg = tq;
+  sa.select_mode = p->select_mode;
+  sa.Hq = p->num_q_heads;
   e = launch_select(sa, s);
   if (e != hipSuccess) return device_status(e, "select kernel launch");
   if (env_log())
@@ -272,7 +278,8 @@ PagedLayout paged_layout(const fp2_params* p, int n, int max_nqb, int max_nkb) {
   const size_t H = p->num_kv_heads, D = p->head_dim;
   size_t off = 0;
   L.qbar = off;
-  off += align_up((size_t)n * H * max_nqb * D * 4);
+  const size_t QH = p->select_mode == 1 ? p->num_q_heads : p->num_kv_heads;
+  off += align_up((size_t)n * QH * max_nqb * D * 4);
   L.kbar = off;
   off += align_up((size_t)n * H * max_nkb * D * 4);
   L.vbar = off;
@@ -374,6 +381,7 @@ static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* 
   pa.D = D;
   pa.block = b;
   pa.fp8 = p->in_dtype == FP2_FP8_E4M3;
+  pa.select_mode = p->select_mode;
   pa.bsum_k = bsum_k;
   pa.bsum_v = bsum_v;
   pa.cached_blocks = cached_blocks;
@@ -390,6 +398,8 @@ static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* 
   sa.block = b;
   sa.tau = p->tau;
   sa.rows_per_wg = tq;
+  sa.select_mode = p->select_mode;
+  sa.Hq = p->num_q_heads;
   e = launch_select(sa, s);
   if (e != hipSuccess) return device_status(e, "select kernel launch");
   PlanArgs pl{};

@@ -48,6 +48,7 @@ struct PoolArgs {
   float* bsum_k;
   float* bsum_v;
   const int* cached_blocks;
+  int select_mode;          // 1: qbar per query head [B, Hq, nqb_stride, D]
 };
 
 struct SelectArgs {
@@ -59,6 +60,8 @@ struct SelectArgs {
   int Hkv, D, block;
   float tau;
   int rows_per_wg;          // query blocks per workgroup
+  int select_mode;          // 0: group-mean qbar; 1: union over the group's query heads
+  int Hq;
 };
 
 // Work-ordered task list of a continuous batch (plan.hip).

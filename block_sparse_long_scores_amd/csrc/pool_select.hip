@@ -107,6 +107,14 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
       }
     }
     __syncthreads();
+    if (a.select_mode == 1) {  // union selection: one mean per query head
+      const float inv1 = 1.f / (float)nr;
+      for (int o = t; o < a.Hq * D; o += kPoolThreads) {
+        const int hq = o / D, dd = o - hq * D;
+        a.qbar[(((long)s * a.Hq + hq) * a.seq.nqb_stride + il) * D + dd] = red[o] * inv1;
+      }
+      return;
+    }
     const int G = a.Hq / a.Hkv;
     const float inv = 1.f / (float)(G * nr);
     for (int o = t; o < a.Hkv * D; o += kPoolThreads) {
@@ -217,58 +225,102 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int D = a.D;
   const int jmax = g.first_qb + il0 + nrows - 1;  // last visible key block of the run
   const int ncols = jmax + 1;
-  float* qb = smem;                 // [TQ][D]
-  float* sc = smem + TQ * D;        // [TQ][ncols]
+  const int nw = (ncols + 31) >> 5;
+  float* qb = smem;                           // [TQ][D]
+  float* sc = smem + TQ * D;                  // [TQ][ncols]
+  uint32_t* kb = (uint32_t*)(sc + TQ * ncols);  // union mode: [TQ][nw] keep bits
   const int t = threadIdx.x;
-  const float* qsrc = a.qbar + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il0) * D;
-  for (int o = t; o < nrows * D; o += kSelThreads) qb[o] = qsrc[o];
-  __syncthreads();
-
-  // scores S[r][j] = <qbar_r, kbar_j> for all j <= jmax (fp32, fixed fma order)
-  const float* kb = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
-  for (int j = t; j < ncols; j += kSelThreads) {
-    float acc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const float4* krow = (const float4*)(kb + (long)j * D);
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      float4 kv = krow[d4];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (r < nrows) {
-          float4 qv = *(const float4*)(qb + r * D + 4 * d4);
-          acc[r] = fmaf(qv.x, kv.x, acc[r]);
-          acc[r] = fmaf(qv.y, kv.y, acc[r]);
-          acc[r] = fmaf(qv.z, kv.z, acc[r]);
-          acc[r] = fmaf(qv.w, kv.w, acc[r]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r < nrows) sc[r * ncols + j] = acc[r];
-  }
-  __syncthreads();
-
-  // per row: max over j <= i, threshold, ascending compaction
   const int wave = t >> 6;
   const int lane = t & 63;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const float* kbh = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
+  // group mean: one pass over the group's pooled query; union: one pass per
+  // query head of the group, each OR-ing its kept blocks into kb
+  const bool uni = a.select_mode == 1;
+  const int npass = uni ? a.Hq / a.Hkv : 1;
+  if (uni)
+    for (int o = t; o < nrows * nw; o += kSelThreads) kb[o] = 0u;
+
+  for (int pass = 0; pass < npass; ++pass) {
+    const float* qsrc = uni ? a.qbar + (((long)s * a.Hq + h * npass + pass) * a.seq.nqb_stride + il0) * D
+                            : a.qbar + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il0) * D;
+    __syncthreads();
+    for (int o = t; o < nrows * D; o += kSelThreads) qb[o] = qsrc[o];
+    __syncthreads();
+
+    // scores S[r][j] = <qbar_r, kbar_j> for all j <= jmax (fp32, fixed fma order)
+    for (int j = t; j < ncols; j += kSelThreads) {
+      float acc[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      const float4* krow = (const float4*)(kbh + (long)j * D);
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        float4 kv = krow[d4];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (r < nrows) {
+            float4 qv = *(const float4*)(qb + r * D + 4 * d4);
+            acc[r] = fmaf(qv.x, kv.x, acc[r]);
+            acc[r] = fmaf(qv.y, kv.y, acc[r]);
+            acc[r] = fmaf(qv.z, kv.z, acc[r]);
+            acc[r] = fmaf(qv.w, kv.w, acc[r]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < nrows) sc[r * ncols + j] = acc[r];
+    }
+    __syncthreads();
+
+    // per row: max over j <= i, threshold; group mean: ascending compaction
+    // right away; union: this head's kept blocks into the row's keep bits
+    for (int r = wave; r < nrows; r += kSelThreads / 64) {
+      const int il = il0 + r;
+      const int i = g.first_qb + il;
+      const float* row = sc + r * ncols;
+      float m = -INFINITY;
+      for (int j = lane; j <= i; j += 64) m = fmaxf(m, row[j]);
+      m = wave_max(m);
+      const float thr = m - a.tau;
+      if (uni) {
+        for (int j0 = 0; j0 <= i; j0 += 64) {
+          const int j = j0 + lane;
+          const uint64_t mask = __ballot(j <= i && row[j] >= thr);
+          if (lane == 0) {
+            kb[r * nw + (j0 >> 5)] |= (uint32_t)mask;
+            if ((j0 >> 5) + 1 < nw) kb[r * nw + (j0 >> 5) + 1] |= (uint32_t)(mask >> 32);
+          }
+        }
+        continue;
+      }
+      int* dst = a.block_idx + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il) * (long)a.seq.nkb_stride;
+      int base = 0;
+      for (int j0 = 0; j0 <= i; j0 += 64) {
+        int j = j0 + lane;
+        bool keep = false;
+        if (j <= i) keep = (row[j] >= thr) || j == 0 || j == i;
+        uint64_t mask = __ballot(keep);
+        if (keep) dst[base + __popcll(mask & lt_mask)] = j;
+        base += __popcll(mask);
+      }
+      if (lane == 0) a.block_cnt[((long)s * a.Hkv + h) * a.seq.nqb_stride + il] = base;
+    }
+  }
+  if (!uni) return;
+
+  // union: ascending compaction of the keep bits, plus sink and diagonal
+  __syncthreads();
   for (int r = wave; r < nrows; r += kSelThreads / 64) {
     const int il = il0 + r;
     const int i = g.first_qb + il;
-    const float* row = sc + r * ncols;
-    float m = -INFINITY;
-    for (int j = lane; j <= i; j += 64) m = fmaxf(m, row[j]);
-    m = wave_max(m);
-    const float thr = m - a.tau;
     int* dst = a.block_idx + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il) * (long)a.seq.nkb_stride;
     int base = 0;
     for (int j0 = 0; j0 <= i; j0 += 64) {
-      int j = j0 + lane;
+      const int j = j0 + lane;
       bool keep = false;
-      if (j <= i) keep = (row[j] >= thr) || j == 0 || j == i;
-      uint64_t mask = __ballot(keep);
+      if (j <= i) keep = ((kb[r * nw + (j >> 5)] >> (j & 31)) & 1u) || j == 0 || j == i;
+      const uint64_t mask = __ballot(keep);
       if (keep) dst[base + __popcll(mask & lt_mask)] = j;
       base += __popcll(mask);
     }
@@ -289,7 +341,7 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   dim3 grid((a.seq.nqb_stride + a.rows_per_wg - 1) / a.rows_per_wg, a.Hkv, a.seq.batch);
-  size_t lds = (size_t)a.rows_per_wg * (a.D + a.seq.nkb_stride) * sizeof(float);
+  size_t lds = (size_t)a.rows_per_wg * (a.D + a.seq.nkb_stride + (a.seq.nkb_stride + 31) / 32) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);

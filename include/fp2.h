@@ -88,6 +88,15 @@ typedef struct {
    * are round-to-nearest-even of out / o_scale, saturated to +-448 (e4m3fn
    * has no infinity).  Must be a positive finite value; ignored otherwise.  */
   const float* o_scale;
+  /* Selection rule under GQA packing (explainer §2.2 PackGQA, with the
+   * block selection of §2.1; the pages leave open how the group's heads
+   * share one mask): 0 = the group-mean qbar of step 1 above;
+   * 1 = per query head: qbar_{hq,i} = mean of head hq's rows of block i,
+   * each head applies step 2 to <qbar_{hq,i}, kbar_j>, and the group keeps
+   * the union of its heads' blocks (plus sink and diagonal).  The masks
+   * stay per KV head, since the group shares one K/V tile.  Mode 1 needs
+   * Hq/Hkv times the pooled-query workspace of mode 0.                     */
+  int32_t select_mode;
 } fp2_params;
 
 /* Number of query blocks a sequence touches: blocks of absolute positions

@@ -57,6 +57,11 @@ def test_workspace_sizes():
     mq, mk = fp2.fp2_paged_mask_dims(p, 16384, 131072)
     assert (mq, mk) == (129, 1024)
     assert fp2.fp2_paged_workspace_size(p, 6, 32768, 131072) > 0
+    # per-query-head selection pools every query head: G = 4 times the pooled queries
+    u = params()
+    u.select_mode = 1
+    assert fp2.fp2_select_workspace_size(u, 1, 1024, 1024) == 4 * 2 * 8 * 128 * 4
+    assert fp2.fp2_paged_workspace_size(u, 6, 32768, 131072) > fp2.fp2_paged_workspace_size(p, 6, 32768, 131072)
 
 
 def test_validation_errors():
@@ -76,6 +81,10 @@ def test_validation_errors():
     p = params()
     p.in_dtype = fp2.FP2_FP8_E4M3
     assert select(p) == fp2.FP2_EINVAL                      # fp8 without scales
+    p = params()
+    p.select_mode = 2
+    assert select(p) == fp2.FP2_EINVAL
+    assert "select_mode" in fp2.last_error()
     p = params()
     p.out_dtype = 7
     assert fp2.fp2_dense_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == fp2.FP2_EUNSUPPORTED
