@@ -12,6 +12,13 @@ the FP8 dense kernel, and the paged-KV continuous batch of six sequences
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-dense]
                     [--no-fp8] [--no-paged]
+
+With --sweep WORKLOAD it instead prints the sparsity/error sweep of that
+workload (bf16): for each target block sparsity a tau is bisected on the
+GPU's own block counts, and the selection + attention time and the relative
+L2 distance of the output to the in-house dense kernel's are reported for
+three variants: group-mean selection with and without the mean correction,
+and per-query-head (union) selection with it.
 """
 
 import argparse
@@ -297,6 +304,41 @@ def paged_leg(fp2, w, tau, steps, warmup, stream, seed):
                 note="select + attention in one call (pool, score, select, attend over 64-token permuted pages)")
 
 
+def sweep(fp2, workload, levels, steps, seed):
+    """Sparsity / error sweep of one bf16 workload (see the module docstring)."""
+    import synth
+    import torch
+    w = synth.WORKLOADS[workload]
+    S, hq, hkv, d, b = w["seqlen"], w["hq"], w["hkv"], w["d"], w["block"]
+    prob = synth.make_problem(w["kind"], seed, S, hq, hkv, d, b)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    q, k, v = (t.to(dev) for t in (prob.q, prob.k, prob.v))
+    L = ContigLayer(fp2, q, k, v, fp2.make_params(hq, hkv, d, b, select_mode="union"), S, hkv, d, b)
+    (dense_ms,), _, _ = timed(stream, [L.dense], 2, 1)
+    rows = []
+    for mode, corr in (("mean", True), ("mean", False), ("union", True)):
+        for target in levels:
+            lo, hi = 0.0, 16.0          # sparsity falls as tau grows
+            for _ in range(24):
+                mid = 0.5 * (lo + hi)
+                L.p = fp2.make_params(hq, hkv, d, b, tau=mid, select_mode=mode)
+                L.select()
+                sp = flops(L.cnt.cpu().numpy(), hq, hkv, d, b, S)["sparsity"]
+                lo, hi = (mid, hi) if sp > target else (lo, mid)
+            L.p = fp2.make_params(hq, hkv, d, b, tau=hi, mean_correction=corr, select_mode=mode)
+            (sel, att), step, _ = timed(stream, [L.select, L.attend], steps, 1)
+            F = flops(L.cnt.cpu().numpy(), hq, hkv, d, b, S)
+            row = dict(select=mode, mean_correction=corr, target=target, tau=round(hi, 5),
+                       block_sparsity=round(F["sparsity"], 4), ms=round(step, 3),
+                       speedup_vs_dense=round(dense_ms / step, 2), rel_l2_vs_dense=L.sparse_vs_dense())
+            rows.append(row)
+            log(f"[sweep] {workload} select={mode} corr={int(corr)} target {target:.2f}: tau {hi:.4f} sparsity "
+                f"{F['sparsity']:.4f} {step:.3f} ms ({dense_ms / step:.2f}x) rel_l2 vs dense {row['rel_l2_vs_dense']}")
+    return dict(sweep=workload, dense_ms=round(dense_ms, 3), rows=rows,
+                data="synthetic (seeded planted-retrieval generator with RoPE; no dataset)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,6 +350,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sweep", metavar="WORKLOAD", default=None,
+                    help="print the sparsity / error sweep of a bf16 workload instead of the benchmark line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times), the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -332,6 +376,10 @@ def main():
     from tests.helpers import tau_table
 
     fp2.load()
+    if args.sweep:
+        levels = (0.5, 0.6, 0.7, 0.8, 0.85, 0.9, 0.95)
+        print(json.dumps(sweep(fp2, args.sweep, levels, max(2, min(args.steps, 5)), args.seed)))
+        return
     taus = tau_table()
     w = synth.WORKLOADS[WORKLOAD]
     S, hq, hkv, d, b = w["seqlen"], w["hq"], w["hkv"], w["d"], w["block"]
