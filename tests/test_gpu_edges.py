@@ -1,0 +1,104 @@
+"""GPU edge cases of the contiguous path against the float64 oracle: the
+sparsest mask the rule allows (tau = -inf keeps only the sink and diagonal
+blocks, so every other visible block goes through the mean correction, over
+several 128-pseudo-key rounds with a partial last one), and single-row
+chunks at the end of a long prefix."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import attention as A
+from tests.helpers import (BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, f64, kept_from_lists, max_abs, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(geo, seed):
+    rng = np.random.default_rng(seed)
+    il = {0, 1, geo.nqb // 2, geo.nqb - 1, int(rng.integers(0, geo.nqb))}
+    return sorted(geo.first_qblock + x for x in il if 0 <= x < geo.nqb)
+
+
+# dropped blocks per row up to nkb - 2: 264 (b 64: four rounds of 64 pseudo-
+# keys + 8) and 311 (b 128: two rounds of 128 + 55); the chunked case starts
+# at block 273
+@pytest.mark.parametrize("S,Sq,hq,hkv,d,b,fp8", [(17000, None, 4, 1, 64, 64, False),
+                                                 (40000, None, 8, 2, 128, 128, False),
+                                                 (40000, 5000, 8, 2, 128, 128, False),
+                                                 (40000, None, 8, 2, 128, 128, True)])
+def test_sink_and_diagonal_only(gpu, S, Sq, hq, hkv, d, b, fp8):
+    pr = synth.make_problem("planted", 3, S, hq, hkv, d, b, seqlen_q=Sq)
+    print(f"[case] tau=-inf planted seed=3 Sk={S} Sq={Sq or S} hq={hq} hkv={hkv} d={d} b={b} fp8={fp8}", flush=True)
+    tau = float("-inf")
+    if fp8:
+        qc, qs = synth.quantize_e4m3(pr.q, 1)
+        kc, ks = synth.quantize_e4m3(pr.k, 1)
+        vc, vs = synth.quantize_e4m3(pr.v, 1)
+        q, k, v, qs_, ks_, vs_ = (t.cuda() for t in (qc, kc, vc, qs, ks, vs))
+        p = gpu.make_params(hq, hkv, d, b, tau=tau, fp8=True, q_scale=qs_, k_scale=ks_, v_scale=vs_)
+        # oracle inputs: the exact dequantized values (decoded from the format)
+        qn = oracle.dequantize(qc.numpy(), qs.numpy(), 1)
+        kn = oracle.dequantize(kc.numpy(), ks.numpy(), 1)
+        vn = oracle.dequantize(vc.numpy(), vs.numpy(), 1)
+    else:
+        q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+        p = gpu.make_params(hq, hkv, d, b, tau=tau)
+        qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    torch.cuda.synchronize()
+    geo = A.geometry(qn.shape[0], kn.shape[0], b)
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    # the mask is fixed by the rule alone: exactly blocks 0 and i
+    want = np.zeros_like(kept_gpu)
+    want[:, :, 0] = True
+    want[:, np.arange(geo.nqb), geo.q_block_ids()] = True
+    assert np.array_equal(kept_gpu, want)
+    qbar, kbar, vbar, n_k = A.pool(qn, kn, vn, hkv, b)
+    blocks = _sample(geo, 3)
+    O, L = A.attend(qn, kn, vn, kept_gpu, kbar, vbar, n_k, hkv, b, 1 / math.sqrt(d), True, q_blocks=blocks)
+    rows = np.concatenate([np.arange(*geo.q_rows(i)) for i in blocks])
+    o = f64(out)[rows]
+    e, m = rel_l2(o, O[rows]), max_abs(o, O[rows])
+    lerr = np.abs(f64(lse[0])[:, rows] - L[:, rows]).max()
+    print(f"[edges] blocks={blocks} max dropped={geo.nkb - 2} rel_l2={e:.2e} max_abs={m:.2e} lse_err={lerr:.2e}",
+          flush=True)
+    assert np.isfinite(o).all()
+    if fp8:
+        assert e < FP8_REL_L2 and lerr < 0.07
+    else:
+        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+
+
+@pytest.mark.parametrize("Sk", [5000, 5121, 5120])
+def test_one_row_chunk_after_long_prefix(gpu, Sk):
+    """A one-row chunk (decode-like row) at the end of a prefix, contiguous
+    layout: a partial last block, a block opened by the row, a full block."""
+    hq, hkv, d, b = 8, 2, 128, 128
+    pr = synth.make_problem("planted", 4, Sk, hq, hkv, d, b, seqlen_q=1)
+    print(f"[case] one-row chunk planted seed=4 Sk={Sk}", flush=True)
+    tau = 0.8
+    p = gpu.make_params(hq, hkv, d, b, tau=tau)
+    q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau)
+    geo = ref["geo"]
+    assert geo.nqb == 1
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    band = A.score_band_mask(ref["S"], ref["thr"])
+    assert not ((kept_gpu != ref["kept"]) & ~band).any()
+    O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+    o = f64(out)
+    e, m = rel_l2(o, O), max_abs(o, O)
+    print(f"[edges] one row Sk={Sk}: kept {int(kept_gpu.sum())} of {hkv * (geo.nkb)} rel_l2={e:.2e} max_abs={m:.2e}",
+          flush=True)
+    assert e < BF16_REL_L2 and m < BF16_MAX_ABS
+    assert np.abs(f64(lse[0]) - L).max() < 2e-2
