@@ -64,6 +64,7 @@ _sz = ctypes.c_size_t
 _SIGS = {
     "fp2_num_q_blocks": (_i32, [_i32, _i32, _i32]),
     "fp2_num_k_blocks": (_i32, [_i32, _i32]),
+    "fp2_max_seqlen_k": (_i32, [_P]),
     "fp2_select_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "fp2_select_blocks": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fp2_sparse_prefill": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -178,6 +179,10 @@ def fp2_status_string(status):
 
 def fp2_last_error():
     return last_error()
+
+
+def fp2_max_seqlen_k(params):
+    return load().fp2_max_seqlen_k(ctypes.byref(params))
 
 
 def fp2_version():

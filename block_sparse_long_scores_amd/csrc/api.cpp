@@ -138,6 +138,23 @@ int32_t fp2_num_k_blocks(int32_t seqlen_k, int32_t block_size) {
   return nk_blocks(seqlen_k, block_size);
 }
 
+int32_t fp2_max_seqlen_k(const fp2_params* p) {
+  if (check_params(p) != FP2_OK) return 0;
+  const int D = p->head_dim, b = p->block_size;
+  const int fp8 = p->in_dtype == FP2_FP8_E4M3;
+  // both limits fall as nkb grows: the selection's score rows and the
+  // attention kernel's correction buffers (dropped-block list) in LDS
+  auto fits = [&](int nkb) { return select_rows_per_wg(D, nkb) > 0 && attn_lds_ok(D, b, nkb, fp8); };
+  if (!fits(1)) return 0;
+  int lo = 1, hi = (1 << 30) / b;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (fits(mid)) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo * b;
+}
+
 size_t fp2_select_workspace_size(const fp2_params* p, int32_t batch, int32_t seqlen_q, int32_t seqlen_k) {
   if (check_params(p) != FP2_OK || check_lengths(batch, seqlen_q, seqlen_k) != FP2_OK) return 0;
   const int nqb = nq_blocks(seqlen_q, seqlen_k, p->block_size);

@@ -1086,7 +1086,12 @@ void attn_kernel(AttnArgs a) {
 
 // LDS of the attention kernel for a given key-block count: the K/V tiles or
 // the correction phase's buffers (whichever is larger), then the copy-offset
-// table (then, at launch, the next-tile broadcast slots).
+// table, then the next-tile broadcast slots.  The compiler reserves a static
+// segment in front of the 1 KB-aligned dynamic buffer, which counts against
+// the workgroup's 160 KB as well.
+constexpr int kSchedLdsBytes = 16;
+constexpr int kStaticLdsBytes = 1024;
+
 template <int D, int BLK, bool F8>
 static size_t attn_lds_dtab(int nkb) {
   using C = Cfg<D, BLK, F8>;
@@ -1095,9 +1100,16 @@ static size_t attn_lds_dtab(int nkb) {
   return corr > lds ? corr : lds;
 }
 
+// the dynamic LDS of a launch
+template <int D, int BLK, bool F8>
+static size_t attn_dyn_lds_bytes(int nkb) {
+  return attn_lds_dtab<D, BLK, F8>(nkb) + Cfg<D, BLK, F8>::DTAB + kSchedLdsBytes;
+}
+
+// the workgroup's whole LDS, static segment included (checked against 160 KB)
 template <int D, int BLK, bool F8>
 static size_t attn_lds_bytes(int nkb) {
-  return attn_lds_dtab<D, BLK, F8>(nkb) + Cfg<D, BLK, F8>::DTAB;
+  return attn_dyn_lds_bytes<D, BLK, F8>(nkb) + kStaticLdsBytes;
 }
 
 static int compute_units() {
@@ -1118,10 +1130,16 @@ static std::atomic<unsigned> g_slot_counter{0};
 template <int D, int BLK, bool F8>
 static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
-  const size_t lds = attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
-  const size_t lds_total = lds + 16;  // + the next-tile broadcast slots
-  if (lds_total > 160 * 1024) return hipErrorInvalidValue;
+  if (attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride) > 160 * 1024) return hipErrorInvalidValue;
   if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
+  static int static_ok = 0;  // 1: the kernel's static segment fits the allowance; -1: it does not
+  if (static_ok == 0) {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8>) != hipSuccess) return hipErrorInvalidValue;
+    static_ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
+  }
+  if (static_ok < 0) return hipErrorInvalidValue;
+  const size_t lds_total = attn_dyn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
   hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_total);
   if (e != hipSuccess) return e;
@@ -1130,7 +1148,7 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   a.ntiles = (int)ntiles;
   a.sched_slot = (int)(g_slot_counter.fetch_add(1) % kSchedSlots);
   a.lds_dtab = (int)attn_lds_dtab<D, BLK, F8>(a0.seq.nkb_stride);
-  a.lds_sched = (int)lds;
+  a.lds_sched = (int)(lds_total - kSchedLdsBytes);
   const long grid = ntiles < compute_units() ? ntiles : compute_units();
   hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, st, a.sched_slot);
   e = hipGetLastError();

@@ -104,6 +104,13 @@ typedef struct {
 int32_t fp2_num_q_blocks(int32_t seqlen_q, int32_t seqlen_k, int32_t block_size);
 int32_t fp2_num_k_blocks(int32_t seqlen_k, int32_t block_size);
 
+/* Largest seqlen_k (per sequence, max_seqlen_k for the paged entry points)
+ * that the kernels accept for these parameters: the selection keeps a row of
+ * scores over every key block in LDS, the attention kernel the dropped-block
+ * list of a query block.  Longer calls return FP2_EUNSUPPORTED.  Returns 0
+ * for invalid parameters.                                                    */
+int32_t fp2_max_seqlen_k(const fp2_params* p);
+
 /* Workspace bytes needed by fp2_select_blocks for this problem size (the
  * pooled query blocks, fp32).  Returns 0 for invalid parameters.             */
 size_t fp2_select_workspace_size(const fp2_params* p, int32_t batch,

@@ -98,6 +98,23 @@ def test_validation_errors():
                                   None) == fp2.FP2_EINVAL   # correction needs pooled blocks
 
 
+def test_longest_sequence_limit():
+    """fp2_max_seqlen_k is the exact edge: one key block more is rejected
+    (before anything is launched) by the attention entry points."""
+    p = params(num_q_heads=32, num_kv_heads=8)
+    m = fp2.fp2_max_seqlen_k(p)
+    assert m > 1 << 21 and m % 128 == 0
+    assert fp2.fp2_max_seqlen_k(params(head_dim=96)) == 0
+    over = m + 128
+    assert fp2.fp2_sparse_prefill(p, 1, 1, over, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                  None) == fp2.FP2_EUNSUPPORTED
+    assert "too long" in fp2.last_error()
+    assert fp2.fp2_dense_prefill(p, 1, 1, over, FAKE, FAKE, FAKE, FAKE, None, None) == fp2.FP2_EUNSUPPORTED
+    npg = over // 64 + 1
+    assert fp2.fp2_sparse_prefill_paged(p, 1, FAKE, FAKE, FAKE, 1, over, FAKE, FAKE, npg, 64, FAKE, npg, FAKE, None,
+                                        None, None, FAKE, 1 << 40, None) == fp2.FP2_EUNSUPPORTED
+
+
 def test_paged_validation_errors():
     p = params()
     args = dict(q=FAKE, cu=FAKE, sk=FAKE, mq=1024, mk=4096, kc=FAKE, vc=FAKE, npages=64, page=64, table=FAKE,

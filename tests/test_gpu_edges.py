@@ -1,8 +1,8 @@
 """GPU edge cases of the contiguous path against the float64 oracle: the
 sparsest mask the rule allows (tau = -inf keeps only the sink and diagonal
 blocks, so every other visible block goes through the mean correction, over
-several 128-pseudo-key rounds with a partial last one), and single-row
-chunks at the end of a long prefix."""
+several 128-pseudo-key rounds with a partial last one), single-row chunks
+at the end of a long prefix, and the longest sequence the kernels accept."""
 
 import math
 
@@ -102,3 +102,35 @@ def test_one_row_chunk_after_long_prefix(gpu, Sk):
           flush=True)
     assert e < BF16_REL_L2 and m < BF16_MAX_ABS
     assert np.abs(f64(lse[0]) - L).max() < 2e-2
+
+
+@pytest.mark.slow
+def test_longest_supported_sequence(gpu):
+    """seqlen_k at fp2_max_seqlen_k (2.41M keys at d 128, b 128: the
+    selection's score row and the correction's dropped-block list at their
+    LDS limits), a ragged 334-row chunk at its end; tau 1.0 and -inf."""
+    hq = hkv = 1
+    d = b = 128
+    Sk = gpu.fp2_max_seqlen_k(gpu.make_params(hq, hkv, d, b))
+    Sq = 334
+    pr = synth.make_problem("planted", 7, Sk, hq, hkv, d, b, seqlen_q=Sq)
+    print(f"[case] longest sequence planted seed=7 Sk={Sk} Sq={Sq}", flush=True)
+    q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+    qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    for tau in (1.0, float("-inf")):
+        p = gpu.make_params(hq, hkv, d, b, tau=tau)
+        idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+        out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+        torch.cuda.synchronize()
+        ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, q_blocks=[])
+        geo = ref["geo"]
+        kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+        band = A.score_band_mask(ref["S"], ref["thr"])
+        assert not ((kept_gpu != ref["kept"]) & ~band).any()
+        O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+        o = f64(out)
+        e, m = rel_l2(o, O), max_abs(o, O)
+        lerr = np.abs(f64(lse[0]) - L).max()
+        print(f"[edges] Sk={Sk} tau={tau}: kept {int(kept_gpu.sum())} of {geo.nkb * geo.nqb} pairs, rel_l2={e:.2e} "
+              f"max_abs={m:.2e} lse_err={lerr:.2e}", flush=True)
+        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
