@@ -11,7 +11,7 @@ import torch
 
 import synth
 from oracle import attention as A
-from tests.helpers import BF16_MAX_ABS, BF16_REL_L2, f64, kept_from_lists, max_abs, rel_l2
+from tests.helpers import BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, f64, kept_from_lists, max_abs, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +104,32 @@ def test_union_paged_matches_oracle_and_contiguous(gpu):
         torch.cuda.synchronize()
         assert torch.equal(c2[0], cnt[s, :, :geo.nqb])
         assert torch.equal(o2, out[cu[s]:cu[s + 1]])
+
+
+def test_union_fp8_matches_oracle(gpu):
+    """e4m3 inputs with per-head scales: the per-head pooled queries take the
+    head's own q scale; masks and outputs against the oracle on the exactly
+    dequantized values."""
+    import oracle
+    hq, hkv, d, b, S, tau = 8, 2, 128, 128, 3000, 0.6
+    pr = synth.make_problem("planted", 8, S, hq, hkv, d, b)
+    print(f"[case] union fp8 planted seed=8 Sk={S} tau={tau}", flush=True)
+    qc, qs = synth.quantize_e4m3(pr.q, 1)
+    kc, ks = synth.quantize_e4m3(pr.k, 1)
+    vc, vs = synth.quantize_e4m3(pr.v, 1)
+    q, k, v, qs_, ks_, vs_ = (t.cuda() for t in (qc, kc, vc, qs, ks, vs))
+    p = gpu.make_params(hq, hkv, d, b, tau=tau, fp8=True, q_scale=qs_, k_scale=ks_, v_scale=vs_, select_mode="union")
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv)
+    torch.cuda.synchronize()
+    qn = oracle.dequantize(qc.numpy(), qs.numpy(), 1)
+    kn = oracle.dequantize(kc.numpy(), ks.numpy(), 1)
+    vn = oracle.dequantize(vc.numpy(), vs.numpy(), 1)
+    ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, q_blocks=[], select_mode="union")
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    flips = _assert_union_mask(kept_gpu, ref, hkv)
+    O, _ = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+    e = rel_l2(f64(out).reshape(O.shape), O)
+    print(f"[union fp8] sparsity={A.sparsity(kept_gpu, geo.q_block_ids()):.3f} flips={flips} rel_l2={e:.2e}", flush=True)
+    assert e < FP8_REL_L2
