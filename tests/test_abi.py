@@ -151,3 +151,15 @@ def test_status_strings():
     assert fp2.status_string(fp2.FP2_OK) == "FP2_OK"
     assert fp2.status_string(fp2.FP2_EWORKSPACE) == "FP2_EWORKSPACE"
     assert fp2.status_string(-99) == "FP2_UNKNOWN"
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

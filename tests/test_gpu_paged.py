@@ -102,7 +102,8 @@ def _same_masks(m1, m2, lo, hi, b):
         assert np.array_equal(k1, k2), s
 
 
-def test_paged_block_sum_cache_chunked_prefill(gpu):
+@pytest.mark.parametrize("mode", ["mean", "union"])
+def test_paged_block_sum_cache_chunked_prefill(gpu, mode):
     """Chunked prefill with the key-block sum cache (fp2_sparse_prefill_paged_
     pooled): each chunk's call reads the sums of the full blocks its earlier
     chunks wrote and must give bit-identical masks, outputs and LSE to the
@@ -110,10 +111,10 @@ def test_paged_block_sum_cache_chunked_prefill(gpu):
     hq, hkv, d, b, page = 8, 2, 128, 128, 64
     L = [2048, 1500]
     bounds = [[0, 700, 1300, 2048], [0, 500, 1000, 1500]]   # chunk ends, not block aligned
-    print(f"[case] block-sum cache L={L} chunks={bounds}", flush=True)
+    print(f"[case] block-sum cache L={L} chunks={bounds} select={mode}", flush=True)
     pb = synth.make_paged(14, L, L, hq, hkv, d, b, page_size=page)
     tau = 0.8
-    p = gpu.make_params(hq, hkv, d, b, tau=tau)
+    p = gpu.make_params(hq, hkv, d, b, tau=tau, select_mode=mode)
     kc, vc, tab = pb.k_cache.cuda(), pb.v_cache.cuda(), pb.page_table.cuda()
     bsk, bsv = gpu.block_sum_cache(p, kc)
     cached = torch.zeros(2, dtype=torch.int32, device="cuda")
