@@ -35,6 +35,12 @@
  *    library allocates no device memory and keeps no pointer after a call.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    default stream).  Buffers must stay valid until the stream has run it.
+ *    Only kernels are enqueued (no memset, copy or host synchronisation), so
+ *    a call can be captured into a HIP graph.  Each attention launch takes
+ *    one of 64 device-side tile-queue counter sets in turn, which its own
+ *    first kernel clears: up to 64 launches may run at once on different
+ *    streams, and a captured launch keeps its set, so one graph must not be
+ *    replayed on two streams at the same time.
  *  - Layouts are row-major.  Contiguous tensors are BSHD: q [B, Sq, Hq, d],
  *    k and v [B, Sk, Hkv, d], out [B, Sq, Hq, d].  Query head hq reads KV
  *    head hq / G.  Query row r of a sequence sits at absolute position
