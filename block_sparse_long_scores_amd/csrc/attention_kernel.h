@@ -701,15 +701,28 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   // so that only two S sets (one per column set) are ever live.  The K
   // operands of superchunk sc+1 are read at the start of stage Y, behind its
   // P V MFMAs; the V operands are double-buffered by superchunk parity.
-  auto run_tile8 = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
+  //
+  // With an even NSC the closing P V of a tile (its last superchunk, column
+  // set 1) is carried into the next tile's first stage X, whose P V slots
+  // are otherwise empty: the V operands, P and its scale byte stay in the
+  // registers below across the block boundary (stage X of superchunk 0
+  // reads exactly the parity the last superchunk wrote).  The first tile of
+  // a pass takes a zero P (and zero V) there, which adds nothing.
+  constexpr bool CARRY8 = C::NSC % 2 == 0;
+  i32x8 vop8[2][C::MT];
+  i32x8 pp8_0, pp8_1;
+  int sb8_0 = 127, sb8_1 = 127;
+  auto run_tile8 = [&](const char* kt, const char* vt, int mode, int dq, bool carry_out) __attribute__((always_inline)) {
     const int kbo = __builtin_amdgcn_readfirstlane((int)(kt - lds));
     const int vbo = __builtin_amdgcn_readfirstlane((int)(vt - lds));
     const char* kbase = lds + kbo;
     const char* vbase = lds + vbo;
     i32x8 kop[2][C::KS8];
-    i32x8 vop[2][C::MT];
-    i32x8 pp0, pp1;
-    int sb0 = 0, sb1 = 0;
+    auto& vop = vop8;
+    auto& pp0 = pp8_0;
+    auto& pp1 = pp8_1;
+    int& sb0 = sb8_0;
+    int& sb1 = sb8_1;
     f32x16 S0[2], S1[2];
     load_kop8(kbase, 0, kop[0]);
     load_kop8(kbase, 1, kop[1]);
@@ -723,7 +736,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       load_vop8(vbase, sc, vop[cp]);
       dma_some(dq);
       __builtin_amdgcn_sched_barrier(0);
-      stage8(S0, 0, sc, mode, pp0, sb0, sc > 0, vop[cp ^ 1], pp1, sb1, 1, true, kop[0], kop[1], 1, S1);
+      stage8(S0, 0, sc, mode, pp0, sb0, sc > 0 || CARRY8, vop[cp ^ 1], pp1, sb1, 1, true, kop[0], kop[1], 1, S1);
       // stage Y
       if (more) {
         load_kop8(kbase, 2 * sc + 2, kop[0]);
@@ -732,13 +745,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       __builtin_amdgcn_sched_barrier(0);
       stage8(S1, 1, sc, mode, pp1, sb1, true, vop[cp], pp0, sb0, 0, more, kop[0], kop[1], 0, S0);
     }
-    pv8(vop[(C::NSC - 1) & 1], pp1, sb1, 1);
+    if (!CARRY8 || !carry_out) pv8(vop[(C::NSC - 1) & 1], pp1, sb1, 1);
   };
 
   // dq: next-block copy ops to issue per chunk (per superchunk in fp8)
   auto run_main = [&](const char* kt, const char* vt, int mode, int dq) __attribute__((always_inline)) {
     if constexpr (F8) {
-      run_tile8(kt, vt, mode, dq);
+      run_tile8(kt, vt, mode, dq, mode == 0);  // the diagonal block (last) closes its own P V
     } else {
       run_tile(kt, vt, C::KC, mode, 0, 0.f, qop, dq);
     }
@@ -793,6 +806,12 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       for (int mt = 0; mt < C::MT; ++mt) O[mt][nt] = f32x16{};
       lsum[nt] = 0.f;
       if constexpr (F8) Lacc[nt] = f32x16{};
+    }
+    if constexpr (F8 && CARRY8) {  // the carried P V of the pass's first block adds nothing
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) vop8[1][mt] = i32x8{};
+      pp8_1 = i32x8{};
+      sb8_1 = 127;
     }
     if (pass > 0) {
       __syncthreads();
