@@ -565,9 +565,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   //  4hh + e%4.  The MFMA's k-block 0 (bytes 0..15 of both lane halves) is
   //  thus exactly the first chunk and k-block 1 the second, and the E8M0
   //  scale of k-block kb of column n is read from lane n + 32kb: P is stored
-  //  per (query, chunk) as P' = P * 2^-b with b chosen from the chunk's max,
-  //  so that P' lies in [128, 256) at the max, and 2^b is applied inside the
-  //  MFMA (no fp8 overflow, full e4m3 precision for the largest terms).
+  //  per (query, superchunk) as P' = P * 2^-b with b chosen from the
+  //  superchunk's max, so that P' lies in [128, 256) at the max, and 2^b is
+  //  applied inside the MFMA (no fp8 overflow, full e4m3 precision for the
+  //  largest terms; both k-blocks carry the same scale byte).
   //  V^T (A side of O^T): ds_read_b64_tr_b8 returns to lane i of a 16-lane
   //  group byte e = byte i%8 of the row addressed by source lane 2e + i/8, so
   //  source lanes 2e, 2e+1 address the same key (the P byte order above) at d
@@ -602,9 +603,11 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   };
   // Superchunk softmax of column set nt (Sn[q] is the S^T chunk 2sc + q), in
   // pieces: sm8_scale(q) applies the causal mask (mode 1) to chunk q and
-  // takes its max and power-of-two scale; sm8_exp(q, j) turns registers
-  // 4j..4j+3 of chunk q into 4 scaled e4m3 bytes of P.
-  auto sm8_scale = [&](f32x16 (&Sn)[2], int q, int nt, int sc, int mode, int (&bq)[2], float (&bias)[2])
+  // takes its max, and for q = 1 the superchunk's power-of-two scale (one
+  // scale per 64 keys: the max-tree tail and the scale arithmetic run once
+  // instead of per chunk); sm8_exp(q, j) turns registers 4j..4j+3 of chunk q
+  // into 4 scaled e4m3 bytes of P.
+  auto sm8_scale = [&](f32x16 (&Sn)[2], int q, int nt, int sc, int mode, float& mh, int& bq, float& bias)
       __attribute__((always_inline)) {
     if (mode == 1) {
 #pragma unroll
@@ -614,24 +617,29 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       }
     }
     // NaN-propagating maximum (v_maximum3_f32, no canonicalizing copies of
-    // the MFMA results, which fmaxf needs in IEEE mode): 16 values in 8 ops,
-    // then the other lane half's 16 keys of the same query column
+    // the MFMA results, which fmaxf needs in IEEE mode): 16 values in 8 ops;
+    // chunk 1 then takes chunk 0's and the other lane half's 16 keys of the
+    // same query column, and sets the superchunk's scale
     const f32x16& v = Sn[q];
     const float m0 = maximum3(v[0], v[1], v[2]), m1 = maximum3(v[3], v[4], v[5]);
     const float m2 = maximum3(v[6], v[7], v[8]), m3 = maximum3(v[9], v[10], v[11]);
     const float m4 = maximum3(v[12], v[13], v[14]);
-    const float m = max_partner32(maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), v[15]));
+    if (q == 0) {
+      mh = maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), v[15]);
+      return;
+    }
+    const float m = max_partner32(maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), mh));
     float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
     fx = fminf(fmaxf(fx, -110.f), 120.f);
-    bq[q] = (int)fx - 7;
-    bias[q] = mref[nt] + (float)bq[q];
+    bq = (int)fx - 7;
+    bias = mref[nt] + (float)bq;
   };
-  auto sm8_exp = [&](const f32x16 (&Sn)[2], int q, int j, int nt, const float (&bias)[2], i32x8& pk)
+  auto sm8_exp = [&](const f32x16 (&Sn)[2], int q, int j, int nt, const float bias, i32x8& pk)
       __attribute__((always_inline)) {
-    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias[q]));
-    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias[q]));
-    const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias[q]));
-    const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias[q]));
+    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias));
+    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias));
+    const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias));
+    const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias));
     // (the first convert's other half is overwritten by the second: x0's
     // own register serves as its old value, no zeroing move)
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
@@ -658,8 +666,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
                     const i32x8 (&k0)[C::KS8], const i32x8 (&k1)[C::KS8], int ntq, f32x16 (&So)[2])
       __attribute__((always_inline)) {
     constexpr int NPVS = C::MT + 1, NSLOT = NPVS + 2 * C::KS8, NPIECE = 10;
-    int bq[2];
-    float bias[2];
+    int bq;
+    float bias, mh;
 #pragma unroll
     for (int g = 0; g < NSLOT; ++g) {
       if constexpr (F8) {
@@ -685,7 +693,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       for (int pc = 0; pc < NPIECE; ++pc) {
         if ((pc < NSLOT ? pc : NSLOT - 1) == g) {
           if (pc < 2) {
-            sm8_scale(Sn, pc, nts, sc, mode, bq, bias);
+            sm8_scale(Sn, pc, nts, sc, mode, mh, bq, bias);
           } else {
             sm8_exp(Sn, (pc - 2) >> 2, (pc - 2) & 3, nts, bias, pk);
           }
@@ -693,7 +701,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    sbyte = 127 + (hh ? bq[1] : bq[0]);
+    sbyte = 127 + bq;
   };
   // The NSC superchunks of one fp8 K/V tile, two stages per superchunk sc:
   //   stage X: PV(sc-1, columns 1), QK(sc, columns 1)    ||  softmax(S_sc, columns 0)
