@@ -213,6 +213,12 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
 
 constexpr int kSelThreads = 256;
 
+// Block selection of TQ consecutive query blocks of one (sequence, KV head)
+// per workgroup: scores against every visible pooled key block in LDS, the
+// max-threshold rule per row, then the kept list in ascending order (with
+// the sink and diagonal blocks).  Group-mean mode scores the group's pooled
+// query once; union mode scores each query head of the group and keeps a
+// block when any head keeps it.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   extern __shared__ float smem[];
   const int s = blockIdx.z;
