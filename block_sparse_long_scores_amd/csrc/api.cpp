@@ -81,6 +81,14 @@ fp2_status check_params(const fp2_params* p) {
     return fail(FP2_EINVAL, "mean_correction=%d must be 0 or 1", p->mean_correction);
   if (p->select_mode != 0 && p->select_mode != 1)
     return fail(FP2_EINVAL, "select_mode=%d must be 0 or 1", p->select_mode);
+  // the pooling kernel's 16-byte tasks per row: a query row of all Hq heads,
+  // a key row of K and V of all Hkv heads
+  const long esz = p->in_dtype == FP2_FP8_E4M3 ? 1 : 2;
+  if ((long)p->num_q_heads * p->head_dim * esz > 16L * kPoolMaxTasks ||
+      2L * p->num_kv_heads * p->head_dim * esz > 16L * kPoolMaxTasks)
+    return fail(FP2_EUNSUPPORTED, "num_q_heads=%d / num_kv_heads=%d too many for head_dim=%d (at most %ld q and %ld kv heads)",
+                p->num_q_heads, p->num_kv_heads, p->head_dim, 16L * kPoolMaxTasks / (p->head_dim * esz),
+                8L * kPoolMaxTasks / (p->head_dim * esz));
   return FP2_OK;
 }
 

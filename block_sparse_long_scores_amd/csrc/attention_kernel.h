@@ -1140,16 +1140,16 @@ static size_t attn_lds_bytes(int nkb) {
 }
 
 static int compute_units() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // zero-initialised (static storage); calls may come from several threads
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   if (dev >= 64) dev = 63;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 static std::atomic<unsigned> g_slot_counter{0};
@@ -1159,13 +1159,16 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
   if (attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride) > 160 * 1024) return hipErrorInvalidValue;
   if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
-  static int static_ok = 0;  // 1: the kernel's static segment fits the allowance; -1: it does not
-  if (static_ok == 0) {
+  // 1: the kernel's static segment fits the allowance; -1: it does not
+  static std::atomic<int> static_ok{0};
+  int ok = static_ok.load(std::memory_order_relaxed);
+  if (ok == 0) {
     hipFuncAttributes fa;
     if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8>) != hipSuccess) return hipErrorInvalidValue;
-    static_ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
+    ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
+    static_ok.store(ok, std::memory_order_relaxed);
   }
-  if (static_ok < 0) return hipErrorInvalidValue;
+  if (ok < 0) return hipErrorInvalidValue;
   const size_t lds_total = attn_dyn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
   hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_total);

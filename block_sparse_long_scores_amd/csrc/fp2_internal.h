@@ -30,6 +30,11 @@ struct KVDesc {
   int page_log2;            // log2(page_size) when paged
 };
 
+// The pooling kernel streams one row of a query block (all Hq heads) or of a
+// key block (K and V of all Hkv heads) per step, 16 bytes per task and at
+// most this many tasks per row (256 threads x 4 chunks each).
+constexpr int kPoolMaxTasks = 1024;
+
 struct PoolArgs {
   SeqDesc seq;
   KVDesc kv;

@@ -24,6 +24,7 @@ namespace fp2 {
 
 constexpr int kPoolThreads = 256;
 constexpr int kMaxChunksPerThread = 4;
+static_assert(kPoolThreads * kMaxChunksPerThread == kPoolMaxTasks, "pool task capacity");
 
 // Accumulate one 16-byte chunk of a row into acc[EPC] (fp32).
 template <int ESZ>
@@ -348,11 +349,9 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   dim3 grid((a.seq.nqb_stride + a.rows_per_wg - 1) / a.rows_per_wg, a.Hkv, a.seq.batch);
   size_t lds = (size_t)a.rows_per_wg * (a.D + a.seq.nkb_stride + (a.seq.nkb_stride + 31) / 32) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
+  const hipError_t e =
+      hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, grid, dim3(kSelThreads), lds, st, a);
   return hipGetLastError();
 }

@@ -50,8 +50,12 @@
  *    fp2_last_error() (thread-local) describes the problem.  A failed launch
  *    returns FP2_EDEVICE.  No C++ exception crosses this interface.
  *  - Supported shapes: head_dim in {64, 128}; block_size in {64, 128};
- *    num_q_heads a positive multiple of num_kv_heads; in_dtype FP2_BF16 or
- *    FP2_FP8_E4M3; out_dtype FP2_BF16, FP2_FP32 or FP2_FP8_E4M3 (with o_scale).
+ *    num_q_heads a positive multiple of num_kv_heads, with num_q_heads *
+ *    head_dim <= 8192 and num_kv_heads * head_dim <= 4096 for bf16 inputs
+ *    (16384 and 8192 for fp8; e.g. up to 64 query and 32 KV heads at d 128
+ *    in bf16); in_dtype FP2_BF16 or FP2_FP8_E4M3; out_dtype FP2_BF16,
+ *    FP2_FP32 or FP2_FP8_E4M3 (with o_scale); seqlen_k up to
+ *    fp2_max_seqlen_k.
  */
 #ifndef FP2_H
 #define FP2_H

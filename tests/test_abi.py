@@ -81,6 +81,12 @@ def test_validation_errors():
     p = params()
     p.in_dtype = fp2.FP2_FP8_E4M3
     assert select(p) == fp2.FP2_EINVAL                      # fp8 without scales
+    # head counts beyond the pooling kernel's row capacity are rejected up front
+    assert select(params(num_q_heads=128, num_kv_heads=8)) == fp2.FP2_EUNSUPPORTED
+    assert "heads" in fp2.last_error()
+    assert select(params(num_q_heads=64, num_kv_heads=64)) == fp2.FP2_EUNSUPPORTED
+    assert fp2.fp2_max_seqlen_k(params(num_q_heads=128, num_kv_heads=8)) == 0
+    assert fp2.fp2_max_seqlen_k(params(num_q_heads=64, num_kv_heads=8)) > 0
     p = params()
     p.select_mode = 2
     assert select(p) == fp2.FP2_EINVAL

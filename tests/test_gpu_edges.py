@@ -134,3 +134,41 @@ def test_longest_supported_sequence(gpu):
         print(f"[edges] Sk={Sk} tau={tau}: kept {int(kept_gpu.sum())} of {geo.nkb * geo.nqb} pairs, rel_l2={e:.2e} "
               f"max_abs={m:.2e} lse_err={lerr:.2e}", flush=True)
         assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+
+
+@pytest.mark.parametrize("hq,hkv,fp8", [(64, 32, False), (128, 64, True)])
+def test_most_heads(gpu, hq, hkv, fp8):
+    """The largest head counts the pooling kernel takes at d 128 (a query
+    row of all heads and a key row of K and V are 1024 16-byte tasks each):
+    masks and outputs against the oracle."""
+    d, b, S, tau = 128, 128, 1500, 0.8
+    pr = synth.make_problem("planted", 9, S, hq, hkv, d, b)
+    print(f"[case] most heads hq={hq} hkv={hkv} fp8={fp8} S={S}", flush=True)
+    if fp8:
+        qc, qs = synth.quantize_e4m3(pr.q, 1)
+        kc, ks = synth.quantize_e4m3(pr.k, 1)
+        vc, vs = synth.quantize_e4m3(pr.v, 1)
+        q, k, v, qs_, ks_, vs_ = (t.cuda() for t in (qc, kc, vc, qs, ks, vs))
+        p = gpu.make_params(hq, hkv, d, b, tau=tau, fp8=True, q_scale=qs_, k_scale=ks_, v_scale=vs_)
+        qn = oracle.dequantize(qc.numpy(), qs.numpy(), 1)
+        kn = oracle.dequantize(kc.numpy(), ks.numpy(), 1)
+        vn = oracle.dequantize(vc.numpy(), vs.numpy(), 1)
+    else:
+        q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+        p = gpu.make_params(hq, hkv, d, b, tau=tau)
+        qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv)
+    torch.cuda.synchronize()
+    ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, q_blocks=[])
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    band = A.score_band_mask(ref["S"], ref["thr"])
+    assert not ((kept_gpu != ref["kept"]) & ~band).any()
+    assert np.abs(f64(pk[0]) - ref["kbar"]).max() < 2e-5 and np.abs(f64(pv[0]) - ref["vbar"]).max() < 2e-5
+    O, _ = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+    o = f64(out).reshape(O.shape)
+    e = rel_l2(o, O)
+    print(f"[edges] hq={hq} hkv={hkv}: sparsity {A.sparsity(kept_gpu, geo.q_block_ids()):.3f} rel_l2={e:.2e}",
+          flush=True)
+    assert e < (FP8_REL_L2 if fp8 else BF16_REL_L2)
