@@ -83,7 +83,10 @@ typedef struct {
   int32_t head_dim;        /* d: 64 or 128                                     */
   int32_t block_size;      /* b: 64 or 128 (the selection granularity)         */
   float softmax_scale;     /* <= 0 means 1/sqrt(head_dim)                      */
-  float tau;               /* threshold; +INFINITY keeps every block; NaN is an error */
+  float tau;               /* threshold on the unscaled block scores S_ij;
+                            * +INFINITY keeps every block; NaN is an error.
+                            * A threshold tau_s on softmax-scaled scores
+                            * (s * S_ij) is tau = tau_s / s.                  */
   int32_t mean_correction; /* 0: drop blocks outright; 1: pseudo-key correction */
   int32_t in_dtype;        /* fp2_dtype of q, k, v: FP2_BF16 or FP2_FP8_E4M3   */
   int32_t out_dtype;       /* fp2_dtype of out: FP2_BF16, FP2_FP32 or FP2_FP8_E4M3 */
