@@ -169,3 +169,40 @@ def test_bench_refuses_several_gpus():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/fp2.h compiles as C99 and a C program links against the
+    library and gets the documented host-side answers (no device calls)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib = fp2.LIB_PATH
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <math.h>
+#include <stdio.h>
+#include "fp2.h"
+int main(void) {
+  fp2_params p = {0};
+  p.num_q_heads = 32; p.num_kv_heads = 8; p.head_dim = 128; p.block_size = 128;
+  p.tau = 1.0f; p.mean_correction = 1; p.in_dtype = FP2_BF16; p.out_dtype = FP2_BF16;
+  if (fp2_num_q_blocks(1024, 1024, 128) != 8) return 1;
+  if (fp2_max_seqlen_k(&p) <= 0) return 2;
+  if (fp2_select_blocks(NULL, 1, 8, 8, 0, 0, 0, 0, 0, 0, 0, 0, 0, NULL) != FP2_EINVAL) return 3;
+  p.tau = NAN;
+  if (fp2_dense_prefill(&p, 1, 8, 8, 0, 0, 0, 0, 0, NULL) != FP2_EINVAL) return 4;
+  printf("%s | %s\n", fp2_version(), fp2_last_error());
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(root, "include"), str(src), lib,
+                        "-lm", f"-Wl,-rpath,{os.path.dirname(lib)}", "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "NaN" in r.stdout
