@@ -1,0 +1,83 @@
+"""GPU parity of the call options against the float64 oracle: the mean
+correction switched off (dropped blocks leave the softmax entirely) and a
+softmax scale other than 1/sqrt(d), in bf16 and fp8, contiguous and paged."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import attention as A
+from tests.helpers import (BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, assert_mask_matches, f64, kept_from_lists, max_abs,
+                           rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(pr, fp8):
+    if not fp8:
+        return [t.cuda() for t in (pr.q, pr.k, pr.v)], {}, (f64(pr.q), f64(pr.k), f64(pr.v))
+    qc, qs = synth.quantize_e4m3(pr.q, 1)
+    kc, ks = synth.quantize_e4m3(pr.k, 1)
+    vc, vs = synth.quantize_e4m3(pr.v, 1)
+    dev = [t.cuda() for t in (qc, kc, vc)]
+    scales = dict(fp8=True, q_scale=qs.cuda(), k_scale=ks.cuda(), v_scale=vs.cuda())
+    ref = tuple(oracle.dequantize(c.numpy(), s.numpy(), 1) for c, s in ((qc, qs), (kc, ks), (vc, vs)))
+    return dev, scales, ref
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("corr,scale", [(False, 0.0), (True, 0.05), (False, 0.2)])
+def test_correction_and_scale_options(gpu, fp8, corr, scale):
+    hq, hkv, d, b, S, Sq, tau = 8, 2, 128, 128, 3000, 2200, 0.6
+    pr = synth.make_problem("planted", 31, S, hq, hkv, d, b, seqlen_q=Sq)
+    print(f"[case] options corr={corr} scale={scale} fp8={fp8} Sk={S} Sq={Sq}", flush=True)
+    (q, k, v), scales, (qn, kn, vn) = _inputs(pr, fp8)
+    p = gpu.make_params(hq, hkv, d, b, tau=tau, softmax_scale=scale, mean_correction=corr, **scales)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    torch.cuda.synchronize()
+    s = scale if scale > 0 else 1 / math.sqrt(d)
+    ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, scale=s, mean_correction=corr, q_blocks=[])
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
+    O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, s, corr)
+    o = f64(out).reshape(O.shape)
+    e, m = rel_l2(o, O), max_abs(o, O)
+    lerr = np.abs(f64(lse[0]) - L).max()
+    print(f"[options] sparsity={A.sparsity(kept_gpu, geo.q_block_ids()):.3f} rel_l2={e:.2e} max_abs={m:.2e} "
+          f"lse_err={lerr:.2e}", flush=True)
+    if fp8:
+        assert e < FP8_REL_L2 and lerr < 0.07
+    else:
+        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+
+
+def test_paged_without_correction(gpu):
+    hq, hkv, d, b, page = 8, 2, 128, 128, 64
+    kv_lens, q_lens = [1500, 2048, 700], [300, 2048, 700]
+    tau = 0.6
+    print(f"[case] paged without correction kv_lens={kv_lens} q_lens={q_lens}", flush=True)
+    pb = synth.make_paged(32, kv_lens, q_lens, hq, hkv, d, b, page_size=page)
+    p = gpu.make_params(hq, hkv, d, b, tau=tau, mean_correction=False)
+    out, (idx, cnt), lse = gpu.sparse_prefill_paged(
+        p, pb.q.cuda(), pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda(), max(q_lens), max(kv_lens), pb.k_cache.cuda(),
+        pb.v_cache.cuda(), pb.page_table.cuda(), export_mask=True, return_lse=True)
+    torch.cuda.synchronize()
+    cu = pb.cu_seqlens_q.numpy()
+    for s_, seq in enumerate(pb.seqs):
+        qn, kn, vn = f64(seq["q"]), f64(seq["k"]), f64(seq["v"])
+        ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, mean_correction=False, q_blocks=[])
+        geo = ref["geo"]
+        kept_gpu = kept_from_lists(idx[s_, :, :geo.nqb], cnt[s_, :, :geo.nqb], geo.nkb)
+        assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
+        O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), False)
+        o = f64(out[cu[s_]:cu[s_ + 1]])
+        e, m = rel_l2(o, O), max_abs(o, O)
+        print(f"[options paged] seq {s_}: rel_l2={e:.2e} max_abs={m:.2e}", flush=True)
+        assert e < BF16_REL_L2 and m < BF16_MAX_ABS
+        assert np.abs(f64(lse[cu[s_]:cu[s_ + 1]]).T - L).max() < 2e-2
