@@ -167,17 +167,19 @@ def test_gqa_wider_group_and_small_blocks(gpu):
         assert e < BF16_REL_L2 and m < BF16_MAX_ABS
 
 
-def test_batch2_matches_per_sequence(gpu):
+@pytest.mark.parametrize("Sq", [None, 700])
+def test_batch2_matches_per_sequence(gpu, Sq):
     hq, hkv, d, b, S = 8, 2, 128, 128, 1024
-    prs = [_case("planted", 10 + s, S, hq, hkv, d, b) for s in range(2)]
+    prs = [_case("planted", 10 + s, S, hq, hkv, d, b, Sq) for s in range(2)]
     q = torch.stack([p.q for p in prs]).cuda()
     k = torch.stack([p.k for p in prs]).cuda()
     v = torch.stack([p.v for p in prs]).cuda()
     p = gpu.make_params(hq, hkv, d, b, tau=1.0)
     idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
-    out = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
     for s in range(2):
         i1, c1, k1, v1 = gpu.select_blocks(p, q[s], k[s], v[s])
-        o1 = gpu.sparse_prefill(p, q[s], k[s], v[s], i1, c1, k1, v1)
+        o1, l1 = gpu.sparse_prefill(p, q[s], k[s], v[s], i1, c1, k1, v1, return_lse=True)
         torch.cuda.synchronize()
         assert torch.equal(c1[0], cnt[s]) and torch.equal(o1, out[s])
+        assert torch.equal(l1[0], lse[s])   # [B, Hq, Sq] rows of sequence s
