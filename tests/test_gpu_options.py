@@ -81,3 +81,36 @@ def test_paged_without_correction(gpu):
         print(f"[options paged] seq {s_}: rel_l2={e:.2e} max_abs={m:.2e}", flush=True)
         assert e < BF16_REL_L2 and m < BF16_MAX_ABS
         assert np.abs(f64(lse[cu[s_]:cu[s_ + 1]]).T - L).max() < 2e-2
+
+
+def test_null_pooled_buffers(gpu):
+    """pooled_v may be NULL for the selection (not written), and both pooled
+    buffers may be NULL for attention without the correction: the same
+    masks and outputs as with the buffers."""
+    hq, hkv, d, b, S, tau = 8, 2, 128, 128, 2000, 0.6
+    pr = synth.make_problem("planted", 33, S, hq, hkv, d, b)
+    print("[case] NULL pooled buffers, S=2000", flush=True)
+    q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+    p = gpu.make_params(hq, hkv, d, b, tau=tau, mean_correction=False)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    ref = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv)
+    nqb, nkb = idx.shape[2], idx.shape[3]
+    idx2 = torch.full_like(idx, -1)
+    cnt2 = torch.empty_like(cnt)
+    pk2 = torch.empty_like(pk)
+    ws = torch.empty(gpu.fp2_select_workspace_size(p, 1, S, S), dtype=torch.uint8, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+    st = gpu.fp2_select_blocks(p, 1, S, S, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx2.data_ptr(), cnt2.data_ptr(),
+                               pk2.data_ptr(), None, ws.data_ptr(), ws.numel(), sh)
+    assert st == gpu.FP2_OK, gpu.last_error()
+    out = torch.empty_like(ref)
+    st = gpu.fp2_sparse_prefill(p, 1, S, S, q.data_ptr(), k.data_ptr(), v.data_ptr(), idx2.data_ptr(), cnt2.data_ptr(),
+                                None, None, out.data_ptr(), None, sh)
+    assert st == gpu.FP2_OK, gpu.last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(cnt2, cnt) and torch.equal(pk2, pk)
+    for h in range(hkv):
+        for il in range(nqb):
+            c = int(cnt[0, h, il])
+            assert torch.equal(idx2[0, h, il, :c], idx[0, h, il, :c])
+    assert torch.equal(out, ref)
