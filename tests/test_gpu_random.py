@@ -1,0 +1,72 @@
+"""Seeded random configurations against the float64 oracle: sequence and
+chunk lengths, GQA ratio, head dim, block size, threshold, precision,
+selection rule and correction drawn per case (a fixed list, the same on
+every run), covering combinations the targeted tests do not."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import attention as A
+from tests.helpers import BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, f64, kept_from_lists, max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _config(seed):
+    r = np.random.default_rng(1000 + seed)
+    d = int(r.choice([64, 128]))
+    b = int(r.choice([64, 128]))
+    hkv = int(r.choice([1, 2, 3]))
+    G = int(r.choice([1, 2, 4, 8]))
+    Sk = int(r.integers(b + 1, 2600))
+    Sq = int(r.integers(1, Sk + 1)) if r.random() < 0.5 else Sk
+    return dict(d=d, b=b, hkv=hkv, hq=G * hkv, Sk=Sk, Sq=Sq, tau=float(r.uniform(0.0, 2.5)),
+                fp8=bool(r.random() < 0.35), union=bool(r.random() < 0.3), corr=bool(r.random() < 0.8),
+                kind=str(r.choice(["planted", "iid"])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_config(gpu, seed):
+    c = _config(seed)
+    print(f"[case] random seed={seed} {c}", flush=True)
+    pr = synth.make_problem(c["kind"], 40 + seed, c["Sk"], c["hq"], c["hkv"], c["d"], c["b"], seqlen_q=c["Sq"])
+    mode = "union" if c["union"] else "mean"
+    if c["fp8"]:
+        qc, qs = synth.quantize_e4m3(pr.q, 1)
+        kc, ks = synth.quantize_e4m3(pr.k, 1)
+        vc, vs = synth.quantize_e4m3(pr.v, 1)
+        q, k, v = (t.cuda() for t in (qc, kc, vc))
+        p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], mean_correction=c["corr"], fp8=True,
+                            q_scale=qs.cuda(), k_scale=ks.cuda(), v_scale=vs.cuda(), select_mode=mode)
+        qn, kn, vn = (oracle.dequantize(x.numpy(), y.numpy(), 1) for x, y in ((qc, qs), (kc, ks), (vc, vs)))
+    else:
+        q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+        p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], mean_correction=c["corr"],
+                            select_mode=mode)
+        qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    torch.cuda.synchronize()
+    ref = A.sparse_prefill(qn, kn, vn, c["hkv"], c["b"], c["tau"], mean_correction=c["corr"], q_blocks=[],
+                           select_mode=mode)
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    band = A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if c["union"] else A.score_band_mask(ref["S"], ref["thr"])
+    assert not ((kept_gpu != ref["kept"]) & ~band).any()
+    O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
+                    1 / math.sqrt(c["d"]), c["corr"])
+    o = f64(out).reshape(O.shape)
+    e, m = rel_l2(o, O), max_abs(o, O)
+    lerr = np.abs(f64(lse[0]) - L).max()
+    print(f"[random] sparsity={A.sparsity(kept_gpu, geo.q_block_ids()):.3f} rel_l2={e:.2e} max_abs={m:.2e} "
+          f"lse_err={lerr:.2e}", flush=True)
+    assert np.isfinite(o).all()
+    if c["fp8"]:
+        assert e < FP8_REL_L2 and lerr < 0.07
+    else:
+        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
