@@ -70,3 +70,60 @@ def test_random_config(gpu, seed):
         assert e < FP8_REL_L2 and lerr < 0.07
     else:
         assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+
+
+def _paged_config(seed):
+    r = np.random.default_rng(2000 + seed)
+    d = int(r.choice([64, 128]))
+    b = int(r.choice([64, 128]))
+    page = int(r.choice([p for p in (16, 32, 64, 128) if p <= b and b // p <= 64]))
+    hkv = int(r.choice([1, 2]))
+    G = int(r.choice([1, 4, 8]))
+    n = int(r.integers(1, 5))
+    kv = [int(r.integers(1, 2500)) for _ in range(n)]
+    ql = [int(r.integers(1, L + 1)) if r.random() < 0.6 else L for L in kv]
+    return dict(d=d, b=b, page=page, hkv=hkv, hq=G * hkv, kv=kv, q=ql, tau=float(r.uniform(0.2, 2.0)),
+                fp8=bool(r.random() < 0.35), union=bool(r.random() < 0.3))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_paged_batch(gpu, seed):
+    c = _paged_config(seed)
+    print(f"[case] random paged seed={seed} {c}", flush=True)
+    pb = synth.make_paged(60 + seed, c["kv"], c["q"], c["hq"], c["hkv"], c["d"], c["b"], page_size=c["page"],
+                          fp8=c["fp8"])
+    mode = "union" if c["union"] else "mean"
+    scales = dict(fp8=True, q_scale=pb.q_scale.cuda(), k_scale=pb.k_scale.cuda(), v_scale=pb.v_scale.cuda()) \
+        if c["fp8"] else {}
+    p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], select_mode=mode, **scales)
+    out, (idx, cnt), lse = gpu.sparse_prefill_paged(
+        p, pb.q.cuda(), pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda(), max(c["q"]), max(c["kv"]), pb.k_cache.cuda(),
+        pb.v_cache.cuda(), pb.page_table.cuda(), export_mask=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "a canary (NaN) page was read"
+    cu = pb.cu_seqlens_q.numpy()
+    for s_, seq in enumerate(pb.seqs):
+        if c["fp8"]:
+            # oracle inputs: the exact dequantized values (decoded from the format)
+            qn = oracle.dequantize(seq["qc"].numpy(), pb.q_scale.numpy(), 1)
+            kn = oracle.dequantize(seq["kc"].numpy(), pb.k_scale.numpy(), 1)
+            vn = oracle.dequantize(seq["vc"].numpy(), pb.v_scale.numpy(), 1)
+        else:
+            qn, kn, vn = f64(seq["q"]), f64(seq["k"]), f64(seq["v"])
+        ref = A.sparse_prefill(qn, kn, vn, c["hkv"], c["b"], c["tau"], q_blocks=[], select_mode=mode)
+        geo = ref["geo"]
+        kept_gpu = kept_from_lists(idx[s_, :, :geo.nqb], cnt[s_, :, :geo.nqb], geo.nkb)
+        band = (A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if c["union"]
+                else A.score_band_mask(ref["S"], ref["thr"]))
+        assert not ((kept_gpu != ref["kept"]) & ~band).any(), s_
+        O, Lr = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
+                         1 / math.sqrt(c["d"]), True)
+        o = f64(out[cu[s_]:cu[s_ + 1]])
+        e, m = rel_l2(o, O), max_abs(o, O)
+        print(f"[random paged] seq {s_}: Sk={c['kv'][s_]} Sq={c['q'][s_]} rel_l2={e:.2e} max_abs={m:.2e}", flush=True)
+        assert np.isfinite(o).all()
+        if c["fp8"]:
+            assert e < FP8_REL_L2
+        else:
+            assert e < BF16_REL_L2 and m < BF16_MAX_ABS
+            assert np.abs(f64(lse[cu[s_]:cu[s_ + 1]]).T - Lr).max() < 2e-2
