@@ -62,6 +62,26 @@ def flops(cnt, hq, hkv, d, b, S):
                 executed_attn=executed_attn, executed_corr=executed_corr, dense_eq=dense_eq, dense_exec=dense_exec)
 
 
+def tau_table():
+    """tau per (workload, target sparsity), bisected on the oracle's float64
+    block scores by tests/golden/make_tau_table.py."""
+    with open(os.path.join(ROOT, "tests", "golden", "tau_table.json")) as f:
+        return json.load(f)["entries"]
+
+
+def blas_info():
+    """(vendor and version, threads) of the BLAS numpy uses on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            return f"{i.get('internal_api', '?')} {i.get('version', '')}".strip(), int(i.get("num_threads", 1))
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", os.cpu_count()
+
+
 def kernel_source_hash():
     """Hash of the HIP sources; HBM traffic read from profiles/ is reported only
     if it was measured on the same sources."""
@@ -94,11 +114,7 @@ def cpu_baseline(prob, hkv, b, tau, budget_s=12.0, seed=0):
     a time, until the time budget is spent; extrapolated to one layer (all KV
     groups, all query blocks, by kept-block count) in ms."""
     from oracle import attention as A
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    blas, threads = blas_info()
     S = prob.q.shape[0]
     G = prob.q.shape[1] // hkv
     q = prob.q[:, :G].float().numpy()
@@ -122,7 +138,8 @@ def cpu_baseline(prob, hkv, b, tau, budget_s=12.0, seed=0):
     kept_rows = kept.sum(axis=2)[0]
     scale_attn = kept_rows.sum() / kept_rows[done].sum()
     per_layer = hkv * ((t2 - t1) + (t3 - t2) * scale_attn)
-    return dict(value=round(float(per_layer) * 1e3, 1), unit="ms/layer (extrapolated)", cores=threads, kind="oracle",
+    return dict(value=round(float(per_layer) * 1e3, 1), unit="ms/layer (extrapolated)", cores=threads, blas=blas,
+                host_cpus=os.cpu_count(), kind="oracle",
                 sample=f"float64 oracle on KV group 0: pool+select over all {geo.nqb} query blocks "
                        f"({t2 - t1:.1f} s) + attention of {len(done)} seeded random query blocks "
                        f"({t3 - t2:.1f} s, {kept_rows[done].sum()} of {kept_rows.sum()} kept blocks); "
@@ -373,7 +390,6 @@ def main():
     import torch
     import block_sparse_long_scores_amd as fp2
     import synth
-    from tests.helpers import tau_table
 
     fp2.load()
     if args.sweep:

@@ -9,7 +9,6 @@ fallback, and a missing library raises ImportError when first used.
 """
 
 import ctypes
-import math
 import os
 
 import torch
@@ -71,6 +70,7 @@ _SIGS = {
     "fp2_dense_prefill": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp2_paged_mask_dims": (None, [_P, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "fp2_paged_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
+    "fp2_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "fp2_sparse_prefill_paged": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp,
                                                 _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fp2_sparse_prefill_paged_pooled": (ctypes.c_int, [_P, _i32, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32,
@@ -151,6 +151,10 @@ def fp2_paged_mask_dims(params, max_seqlen_q, max_seqlen_k):
 
 def fp2_paged_workspace_size(params, num_seqs, max_seqlen_q, max_seqlen_k):
     return load().fp2_paged_workspace_size(ctypes.byref(params), num_seqs, max_seqlen_q, max_seqlen_k)
+
+
+def fp2_workspace_size(params, batch, max_seqlen_q, max_seqlen_k):
+    return load().fp2_workspace_size(ctypes.byref(params), batch, max_seqlen_q, max_seqlen_k)
 
 
 def fp2_sparse_prefill_paged(params, num_seqs, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_seqlen_k, k_cache,
@@ -335,6 +339,3 @@ def sparse_prefill_paged(params, q, cu_seqlens_q, seqlens_k, max_seqlen_q, max_s
         res.append(lse)
     return res[0] if len(res) == 1 else tuple(res)
 
-
-def default_scale(head_dim):
-    return 1.0 / math.sqrt(head_dim)

@@ -397,7 +397,9 @@ static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* 
   pa.q = q;
   pa.qbar = qbar;
   pa.kbar = kbar;
-  pa.vbar = vbar;
+  // the value means (and their cached sums) are needed only by the mean
+  // correction; without it the pool kernel reads and writes no V at all
+  pa.vbar = p->mean_correction ? vbar : nullptr;
   pa.q_scale = p->q_scale;
   pa.k_scale = p->k_scale;
   pa.v_scale = p->v_scale;
@@ -460,6 +462,18 @@ static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* 
     fprintf(stderr, "[fp2] paged n=%d max_sq=%d max_sk=%d page=%d max_nqb=%d max_nkb=%d\n", num_seqs, max_seqlen_q,
             max_seqlen_k, page_size, max_nqb, max_nkb);
   return ok();
+}
+
+size_t fp2_workspace_size(const fp2_params* p, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k) {
+  if (check_params(p) != FP2_OK || check_lengths(batch, max_seqlen_q, max_seqlen_k) != FP2_OK) return 0;
+  int nq, nk;
+  fp2_paged_mask_dims(p, max_seqlen_q, max_seqlen_k, &nq, &nk);
+  // the pooled-query region of the paged layout is the select workspace of
+  // the largest query-block count any (sq <= max_sq, sk <= max_sk) reaches
+  const size_t paged = paged_layout(p, batch, nq, nk).total;
+  const size_t qh = p->select_mode == 1 ? p->num_q_heads : p->num_kv_heads;
+  const size_t sel = align_up((size_t)batch * qh * nq * p->head_dim * sizeof(float));
+  return paged > sel ? paged : sel;
 }
 
 fp2_status fp2_sparse_prefill_paged(const fp2_params* p, int32_t num_seqs, const void* q, const int32_t* cu_seqlens_q,

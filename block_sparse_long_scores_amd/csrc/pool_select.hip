@@ -147,7 +147,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   float* csk = nullptr;
   float* csv = nullptr;
   bool from_cache = false;
-  if (a.bsum_k && c1 - c0 == a.block) {
+  // (a cache without V sums serves only calls that pool no V: the V tasks
+  // would otherwise read or write through a NULL pointer)
+  if (a.bsum_k && (a.bsum_v || !a.vbar) && c1 - c0 == a.block) {
     const long pg = a.kv.page_table[(long)s * a.kv.max_pages + (c0 >> a.kv.page_log2)];
     csk = a.bsum_k + pg * W;
     csv = a.bsum_v ? a.bsum_v + pg * W : nullptr;

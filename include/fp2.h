@@ -129,6 +129,15 @@ int32_t fp2_max_seqlen_k(const fp2_params* p);
 size_t fp2_select_workspace_size(const fp2_params* p, int32_t batch,
                                  int32_t seqlen_q, int32_t seqlen_k);
 
+/* One workspace size for every entry point that takes a workspace: at least
+ * fp2_select_workspace_size(p, b, sq, sk) for every b <= batch, sq <=
+ * max_seqlen_q, sk <= max_seqlen_k (sq <= sk), and at least
+ * fp2_paged_workspace_size(p, n, max_seqlen_q, max_seqlen_k) for every
+ * n <= batch.  A caller that sizes one buffer for the largest call it will
+ * make can use it for both paths.  Returns 0 for invalid parameters.        */
+size_t fp2_workspace_size(const fp2_params* p, int32_t batch,
+                          int32_t max_seqlen_q, int32_t max_seqlen_k);
+
 /* Block selection (steps 1-2 above; abstract: pattern discovery and max-based
  * dynamic thresholding; explainer §2.1: Supp(q)).
  *   q, k, v    : contiguous BSHD inputs (in_dtype).

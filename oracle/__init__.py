@@ -41,7 +41,6 @@ from .attention import (  # noqa: F401
     sparse_prefill,
     correction_split,
     sparsity,
-    kept_lists,
     score_band_mask,
 )
 from .e4m3 import e4m3_decode, e4m3_encode, dequantize  # noqa: F401

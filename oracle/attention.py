@@ -163,15 +163,6 @@ def union_band_mask(S_heads, thr_heads, num_kv_heads, band=1e-3):
     return b.reshape(num_kv_heads, G, *b.shape[1:]).any(axis=1)
 
 
-def kept_lists(kept):
-    """Ascending kept-block list and count per (h, il), for comparison with a
-    compacted index list."""
-    H, nq, _ = kept.shape
-    lists = [[np.flatnonzero(kept[h, il]) for il in range(nq)] for h in range(H)]
-    cnt = kept.sum(axis=2).astype(np.int64)
-    return lists, cnt
-
-
 def score_band_mask(S, thr, band=1e-3):
     """True where a block's score lies within ``band`` of its row threshold:
     the only places where two correct selections may differ."""

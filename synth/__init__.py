@@ -168,13 +168,6 @@ def quantize_e4m3(x, head_axis, scale=None):
     return codes.contiguous(), scale.float().contiguous()
 
 
-def dequant_e4m3_torch(codes, scale, head_axis):
-    """Library-side dequantization (torch cast) used to feed bf16 references."""
-    shape = [1] * codes.dim()
-    shape[head_axis] = -1
-    return codes.view(torch.float8_e4m3fn).float() * scale.reshape(shape)
-
-
 # ---------------------------------------------------------------- paged KV
 
 @dataclass

@@ -36,6 +36,57 @@ def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
 
 
+BF16_LSE_ABS = 2e-2    # LSE tolerance, bf16 path
+FP8_LSE_ABS = 0.07     # LSE tolerance, fp8 path: e4m3 rounding of P, ln(1 + 2^-4) = 0.061
+
+
+def block_errors(o, O, geo, hkv, blocks=None, lse=None, L=None):
+    """Errors of every (query block, KV head) pair on its own: the rows of
+    query block i (absolute id) and the G query heads of KV head h.
+    o, O [Sq, Hq, d]; lse, L [Hq, Sq] (optional).  Returns a list of dicts
+    with block, head, rows, rel_l2, max_abs and lse_err."""
+    o = np.asarray(o, np.float64).reshape(O.shape)
+    G = O.shape[1] // hkv
+    ids = geo.q_block_ids() if blocks is None else blocks
+    res = []
+    for i in ids:
+        r0, r1 = geo.q_rows(int(i))
+        for h in range(hkv):
+            a, b = o[r0:r1, h * G:(h + 1) * G], O[r0:r1, h * G:(h + 1) * G]
+            e = dict(block=int(i), head=h, rows=r1 - r0, rel_l2=rel_l2(a, b), max_abs=max_abs(a, b),
+                     finite=bool(np.isfinite(a).all()), lse_err=0.0)
+            if lse is not None:
+                e["lse_err"] = float(np.abs(np.asarray(lse, np.float64)[h * G:(h + 1) * G, r0:r1]
+                                            - L[h * G:(h + 1) * G, r0:r1]).max())
+            res.append(e)
+    return res
+
+
+def check_blocks(o, O, geo, hkv, fp8=False, blocks=None, lse=None, L=None, label="parity", rel_tol=None):
+    """Hold every (query block, KV head) pair to the output tolerance on its
+    own (rel-L2 <= 1e-2 and max-abs <= 2e-2 in bf16, rel-L2 <= 5e-2 in fp8;
+    LSE within 2e-2 / 0.07), so that large outputs of one block (the first
+    query blocks attend to few keys) cannot hide the error of another.
+    Prints the worst pair and the last block; returns the error list."""
+    errs = block_errors(o, O, geo, hkv, blocks, lse, L)
+    tol = rel_tol if rel_tol is not None else (FP8_REL_L2 if fp8 else BF16_REL_L2)
+    lse_tol = FP8_LSE_ABS if fp8 else BF16_LSE_ABS
+    wr = max(errs, key=lambda e: e["rel_l2"])
+    wa = max(errs, key=lambda e: e["max_abs"])
+    last = max(e["block"] for e in errs)
+    lastr = max(e["rel_l2"] for e in errs if e["block"] == last)
+    msg = (f"[{label}] {len(errs)} (q-block, kv-head) pairs: worst rel_l2 {wr['rel_l2']:.2e} (block {wr['block']} "
+           f"head {wr['head']}), worst max_abs {wa['max_abs']:.2e} (block {wa['block']} head {wa['head']}), "
+           f"last block {last} rel_l2 {lastr:.2e}")
+    if lse is not None:
+        msg += f", worst lse_err {max(e['lse_err'] for e in errs):.2e}"
+    print(msg, flush=True)
+    bad = [e for e in errs if not (e["finite"] and e["rel_l2"] < tol and (fp8 or e["max_abs"] < BF16_MAX_ABS)
+                                   and e["lse_err"] < lse_tol)]
+    assert not bad, f"{len(bad)} of {len(errs)} (block, head) pairs over tolerance, first: {bad[:4]}"
+    return errs
+
+
 def kept_from_lists(idx, cnt, nkb):
     """GPU (block_idx, block_cnt) of one sequence [Hkv, nqb, nkb] / [Hkv, nqb]
     -> bool mask; also checks the lists are strictly ascending."""

@@ -64,6 +64,27 @@ def test_workspace_sizes():
     assert fp2.fp2_paged_workspace_size(u, 6, 32768, 131072) > fp2.fp2_paged_workspace_size(p, 6, 32768, 131072)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_one_workspace_size_covers_both_paths(mode):
+    """fp2_workspace_size(p, batch, max_sq, max_sk) is at least the select
+    workspace of every smaller call and the paged workspace of every smaller
+    batch; it is 0 for invalid parameters."""
+    p = params()
+    p.select_mode = mode
+    for B, msq, msk in [(1, 131072, 131072), (6, 32768, 131072), (3, 1000, 5000), (2, 1, 129)]:
+        w = fp2.fp2_workspace_size(p, B, msq, msk)
+        assert w > 0 and w % 256 == 0
+        for b in range(1, B + 1):
+            assert w >= fp2.fp2_paged_workspace_size(p, b, msq, msk)
+        for sk in sorted({msk, max(msq, msk - 1), max(msq, msk - 127), msq}):
+            for sq in sorted({msq, max(1, msq - 1), max(1, msq // 2), 1, 129, 128}):
+                if sq <= min(msq, sk):
+                    assert w >= fp2.fp2_select_workspace_size(p, B, sq, sk), (B, sq, sk)
+    assert fp2.fp2_workspace_size(params(head_dim=96), 1, 1024, 1024) == 0
+    assert fp2.fp2_workspace_size(p, 0, 1024, 1024) == 0
+    assert fp2.fp2_workspace_size(p, 1, 2048, 1024) == 0
+
+
 def test_validation_errors():
     lib = fp2.load()
     assert lib.fp2_select_blocks(None, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == fp2.FP2_EINVAL

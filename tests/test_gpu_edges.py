@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from oracle import attention as A
-from tests.helpers import (BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, f64, kept_from_lists, max_abs, rel_l2)
+from tests.helpers import check_blocks, f64, kept_from_lists
 
 pytestmark = pytest.mark.gpu
 
@@ -62,17 +62,8 @@ def test_sink_and_diagonal_only(gpu, S, Sq, hq, hkv, d, b, fp8):
     qbar, kbar, vbar, n_k = A.pool(qn, kn, vn, hkv, b)
     blocks = _sample(geo, 3)
     O, L = A.attend(qn, kn, vn, kept_gpu, kbar, vbar, n_k, hkv, b, 1 / math.sqrt(d), True, q_blocks=blocks)
-    rows = np.concatenate([np.arange(*geo.q_rows(i)) for i in blocks])
-    o = f64(out)[rows]
-    e, m = rel_l2(o, O[rows]), max_abs(o, O[rows])
-    lerr = np.abs(f64(lse[0])[:, rows] - L[:, rows]).max()
-    print(f"[edges] blocks={blocks} max dropped={geo.nkb - 2} rel_l2={e:.2e} max_abs={m:.2e} lse_err={lerr:.2e}",
-          flush=True)
-    assert np.isfinite(o).all()
-    if fp8:
-        assert e < FP8_REL_L2 and lerr < 0.07
-    else:
-        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+    print(f"[edges] blocks={blocks} max dropped={geo.nkb - 2}", flush=True)
+    check_blocks(f64(out), O, geo, hkv, fp8=fp8, blocks=blocks, lse=f64(lse[0]), L=L, label="sink+diagonal only")
 
 
 @pytest.mark.parametrize("Sk", [5000, 5121, 5120])
@@ -96,12 +87,8 @@ def test_one_row_chunk_after_long_prefix(gpu, Sk):
     band = A.score_band_mask(ref["S"], ref["thr"])
     assert not ((kept_gpu != ref["kept"]) & ~band).any()
     O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
-    o = f64(out)
-    e, m = rel_l2(o, O), max_abs(o, O)
-    print(f"[edges] one row Sk={Sk}: kept {int(kept_gpu.sum())} of {hkv * (geo.nkb)} rel_l2={e:.2e} max_abs={m:.2e}",
-          flush=True)
-    assert e < BF16_REL_L2 and m < BF16_MAX_ABS
-    assert np.abs(f64(lse[0]) - L).max() < 2e-2
+    print(f"[edges] one row Sk={Sk}: kept {int(kept_gpu.sum())} of {hkv * (geo.nkb)}", flush=True)
+    check_blocks(f64(out), O, geo, hkv, lse=f64(lse[0]), L=L, label="one-row chunk")
 
 
 @pytest.mark.slow
@@ -128,12 +115,8 @@ def test_longest_supported_sequence(gpu):
         band = A.score_band_mask(ref["S"], ref["thr"])
         assert not ((kept_gpu != ref["kept"]) & ~band).any()
         O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
-        o = f64(out)
-        e, m = rel_l2(o, O), max_abs(o, O)
-        lerr = np.abs(f64(lse[0]) - L).max()
-        print(f"[edges] Sk={Sk} tau={tau}: kept {int(kept_gpu.sum())} of {geo.nkb * geo.nqb} pairs, rel_l2={e:.2e} "
-              f"max_abs={m:.2e} lse_err={lerr:.2e}", flush=True)
-        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+        print(f"[edges] Sk={Sk} tau={tau}: kept {int(kept_gpu.sum())} of {geo.nkb * geo.nqb} pairs", flush=True)
+        check_blocks(f64(out), O, geo, hkv, lse=f64(lse[0]), L=L, label=f"longest tau={tau}")
 
 
 @pytest.mark.parametrize("hq,hkv,fp8", [(64, 32, False), (128, 64, True)])
@@ -167,8 +150,5 @@ def test_most_heads(gpu, hq, hkv, fp8):
     assert not ((kept_gpu != ref["kept"]) & ~band).any()
     assert np.abs(f64(pk[0]) - ref["kbar"]).max() < 2e-5 and np.abs(f64(pv[0]) - ref["vbar"]).max() < 2e-5
     O, _ = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
-    o = f64(out).reshape(O.shape)
-    e = rel_l2(o, O)
-    print(f"[edges] hq={hq} hkv={hkv}: sparsity {A.sparsity(kept_gpu, geo.q_block_ids()):.3f} rel_l2={e:.2e}",
-          flush=True)
-    assert e < (FP8_REL_L2 if fp8 else BF16_REL_L2)
+    print(f"[edges] hq={hq} hkv={hkv}: sparsity {A.sparsity(kept_gpu, geo.q_block_ids()):.3f}", flush=True)
+    check_blocks(f64(out), O, geo, hkv, fp8=fp8, label=f"most heads hq={hq}")

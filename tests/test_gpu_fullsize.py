@@ -1,10 +1,12 @@
 """GPU parity at the full sizes of the benchmark workloads (32K and 128K
 layers in bf16, the 128K layer in FP8, the paged six-sequence batch), in the
 launch configuration bench.py times: the whole layer runs on the GPU through
-the C ABI; the float64 oracle then checks two KV groups, each on its own
-(pool, score and select over the whole sequence -> the group's full block
-mask; attention of sampled query blocks under the GPU's mask -> those rows
-of the output and their LSE)."""
+the C ABI; the float64 oracle then checks every KV group on its own (pool,
+score and select over the whole sequence -> the group's full block mask;
+attention under the GPU's mask of every query block at 32K and of 16 sampled
+query blocks at 128K, the first and the last among them -> those rows of the
+output and their LSE), each (query block, KV head) held to the tolerance on
+its own."""
 
 import math
 
@@ -15,43 +17,38 @@ import torch
 import oracle
 import synth
 from oracle import attention as A
-from tests.helpers import (BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, assert_mask_matches, kept_from_lists, max_abs,
-                           rel_l2, tau_table)
+from tests.helpers import assert_mask_matches, check_blocks, kept_from_lists, tau_table
 
-pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
-FP8_LSE_ABS = 0.07  # ln(1 + 2^-4): e4m3 rounding of P (see test_gpu_fp8)
+N_SAMPLED = 16   # query blocks per KV head checked at 128K
 
 
-def _sample_blocks(nqb, first_qb, seed):
+def _sample_blocks(nqb, first_qb, seed, n=N_SAMPLED):
+    """n seeded query blocks of a sequence (local ids 0 .. nqb-1), always
+    including the first and the last; all of them when nqb <= n."""
+    if nqb <= n:
+        return [first_qb + x for x in range(nqb)]
     rng = np.random.default_rng(seed)
-    il = sorted({nqb - 1, nqb // 2, 0, int(rng.integers(1, max(nqb - 1, 2)))})
-    return [first_qb + x for x in il if 0 <= x < nqb]
+    mid = rng.choice(np.arange(1, nqb - 1), size=n - 2, replace=False)
+    return [first_qb + int(x) for x in sorted({0, nqb - 1, *mid.tolist()})]
 
 
-def _check_group(h, G, q, k, v, tau, b, idx, cnt, out, lse, fp8, seed, label):
+def _check_group(h, G, q, k, v, tau, b, idx, cnt, out, lse, fp8, seed, label, all_blocks=False):
     """q [Sq, G, d], k/v [Sk, 1, d] float64 of KV group h; idx/cnt the GPU
     lists of that group; out [Sq, G, d] and lse [G, Sq] the GPU results."""
     ref = A.sparse_prefill(q, k, v, 1, b, tau, q_blocks=[])
     geo = ref["geo"]
     kept_gpu = kept_from_lists(idx[None], cnt[None], geo.nkb)
     flips = assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
-    blocks = _sample_blocks(geo.nqb, geo.first_qblock, seed)
+    blocks = (list(geo.q_block_ids()) if all_blocks else _sample_blocks(geo.nqb, geo.first_qblock, seed))
     d = q.shape[2]
     O, L = A.attend(q, k, v, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], 1, b, 1 / math.sqrt(d), True,
                     q_blocks=blocks)
-    rows = np.concatenate([np.arange(*geo.q_rows(i)) for i in blocks])
-    o = out[rows]
-    e, m = rel_l2(o, O[rows]), max_abs(o, O[rows])
-    lerr = np.abs(lse[:, rows] - L[:, rows]).max()
     sp = A.sparsity(kept_gpu, geo.q_block_ids())
-    print(f"[{label} h={h}] nqb={geo.nqb} sparsity={sp:.3f} band flips={flips} blocks={blocks} "
-          f"rel_l2={e:.2e} max_abs={m:.2e} lse_err={lerr:.2e}", flush=True)
-    assert np.isfinite(o).all()
-    if fp8:
-        assert e < FP8_REL_L2 and lerr < FP8_LSE_ABS
-    else:
-        assert e < BF16_REL_L2 and m < BF16_MAX_ABS and lerr < 2e-2
+    print(f"[{label} h={h}] nqb={geo.nqb} sparsity={sp:.3f} band flips={flips} blocks checked={len(blocks)}",
+          flush=True)
+    check_blocks(out, O, geo, 1, fp8=fp8, blocks=blocks, lse=lse, L=L, label=f"{label} h={h}")
     return ref
 
 
@@ -84,7 +81,7 @@ def test_fullsize_contiguous(gpu, workload, fp8, sparsity):
     pk_h = pk[0].double().cpu().numpy()
     del out, lse, idx, cnt, pk, pv, dev, qd, kd, vd
     torch.cuda.empty_cache()
-    for h in (0, hkv - 1):
+    for h in range(hkv):
         sl = slice(h * G, (h + 1) * G)
         if fp8:
             q = oracle.dequantize(qc[:, sl].numpy(), qs[sl].numpy(), 1)
@@ -94,7 +91,8 @@ def test_fullsize_contiguous(gpu, workload, fp8, sparsity):
             q = prob.q[:, sl].double().numpy()
             k = prob.k[:, h:h + 1].double().numpy()
             v = prob.v[:, h:h + 1].double().numpy()
-        ref = _check_group(h, G, q, k, v, tau, b, idx_h[h], cnt_h[h], out_h[:, sl], lse_h[sl], fp8, h, workload)
+        ref = _check_group(h, G, q, k, v, tau, b, idx_h[h], cnt_h[h], out_h[:, sl], lse_h[sl], fp8, h, workload,
+                           all_blocks=S <= 32768)
         assert np.abs(pk_h[h] - ref["kbar"][0]).max() < 2e-5
 
 
@@ -117,11 +115,11 @@ def test_fullsize_paged_batch6(gpu):
     cu = pb.cu_seqlens_q.numpy()
     G = hq // hkv
     for s, seq in enumerate(pb.seqs):
-        h = (3 * s + 1) % hkv
-        sl = slice(h * G, (h + 1) * G)
-        q = seq["q"][:, sl].double().numpy()
-        k = seq["k"][:, h:h + 1].double().numpy()
-        v = seq["v"][:, h:h + 1].double().numpy()
-        nqb = A.geometry(q.shape[0], k.shape[0], b).nqb
-        _check_group(h, G, q, k, v, tau, b, idx_h[s, h, :nqb], cnt_h[s, h, :nqb], out_h[cu[s]:cu[s + 1], sl],
-                     lse_h[cu[s]:cu[s + 1], sl].T, False, s, f"paged seq {s}")
+        for h in range(hkv):
+            sl = slice(h * G, (h + 1) * G)
+            q = seq["q"][:, sl].double().numpy()
+            k = seq["k"][:, h:h + 1].double().numpy()
+            v = seq["v"][:, h:h + 1].double().numpy()
+            nqb = A.geometry(q.shape[0], k.shape[0], b).nqb
+            _check_group(h, G, q, k, v, tau, b, idx_h[s, h, :nqb], cnt_h[s, h, :nqb], out_h[cu[s]:cu[s + 1], sl],
+                         lse_h[cu[s]:cu[s + 1], sl].T, False, 100 * s + h, f"paged seq {s}")

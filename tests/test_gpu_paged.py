@@ -9,7 +9,7 @@ import torch
 
 import synth
 from oracle import attention as A
-from tests.helpers import (BF16_MAX_ABS, BF16_REL_L2, assert_mask_matches, f64, kept_from_lists, max_abs, rel_l2)
+from tests.helpers import assert_mask_matches, check_blocks, f64, kept_from_lists
 
 pytestmark = pytest.mark.gpu
 
@@ -41,12 +41,9 @@ def test_paged_matches_oracle_and_contiguous(gpu, d, b, page):
         kept_gpu = kept_from_lists(idx[s, :, :geo.nqb], cnt[s, :, :geo.nqb], geo.nkb)
         assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
         O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
-        o = f64(out[cu[s]:cu[s + 1]])
-        e, m = rel_l2(o, O), max_abs(o, O)
-        print(f"[paged] seq {s}: nqb={geo.nqb} sparsity={A.sparsity(kept_gpu, geo.q_block_ids()):.3f} "
-              f"rel_l2={e:.2e} max_abs={m:.2e}", flush=True)
-        assert e < BF16_REL_L2 and m < BF16_MAX_ABS
-        assert np.abs(f64(lse[cu[s]:cu[s + 1]]).T - L).max() < 2e-2
+        print(f"[paged] seq {s}: nqb={geo.nqb} sparsity={A.sparsity(kept_gpu, geo.q_block_ids()):.3f}", flush=True)
+        check_blocks(f64(out[cu[s]:cu[s + 1]]), O, geo, hkv, lse=f64(lse[cu[s]:cu[s + 1]]).T, L=L,
+                     label=f"paged seq {s}")
         # the contiguous path on the same data gives bit-identical rows
         qc, kc, vc = seq["q"].cuda(), seq["k"].cuda(), seq["v"].cuda()
         i2, c2, pk2, pv2 = gpu.select_blocks(p, qc, kc, vc)
@@ -82,12 +79,9 @@ def test_paged_mixed_prefill_and_decode_rows(gpu):
         kept_gpu = kept_from_lists(idx[s, :, :geo.nqb], cnt[s, :, :geo.nqb], geo.nkb)
         assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
         O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
-        o = f64(out[cu[s]:cu[s + 1]])
-        e, m = rel_l2(o, O), max_abs(o, O)
-        print(f"[mixed] seq {s}: q_len={q_lens[s]} nqb={geo.nqb} kept={int(kept_gpu.sum())} rel_l2={e:.2e} "
-              f"max_abs={m:.2e}", flush=True)
-        assert e < BF16_REL_L2 and m < BF16_MAX_ABS
-        assert np.abs(f64(lse[cu[s]:cu[s + 1]]).T - L).max() < 2e-2
+        print(f"[mixed] seq {s}: q_len={q_lens[s]} nqb={geo.nqb} kept={int(kept_gpu.sum())}", flush=True)
+        check_blocks(f64(out[cu[s]:cu[s + 1]]), O, geo, hkv, lse=f64(lse[cu[s]:cu[s + 1]]).T, L=L,
+                     label=f"mixed seq {s}")
 
 
 def _same_masks(m1, m2, lo, hi, b):
@@ -100,6 +94,23 @@ def _same_masks(m1, m2, lo, hi, b):
         k1 = kept_from_lists(m1[0][s, :, :geo.nqb], c1, geo.nkb)
         k2 = kept_from_lists(m2[0][s, :, :geo.nqb], c2, geo.nkb)
         assert np.array_equal(k1, k2), s
+
+
+def _chunk_vs_oracle(seq, lo, hi, hkv, b, tau, mode, corr, o, lse, idx, cnt, label):
+    """The rows [lo, hi) of one sequence (a chunk over the cached prefix
+    [0, lo)) against the oracle: mask bit-exact outside the band, outputs and
+    LSE per (query block, KV head) under the exported mask."""
+    qn, kn, vn = f64(seq["q"][lo:hi]), f64(seq["k"][:hi]), f64(seq["v"][:hi])
+    d = qn.shape[2]
+    ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, mean_correction=corr, q_blocks=[], select_mode=mode)
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[:, :geo.nqb], cnt[:, :geo.nqb], geo.nkb)
+    band = (A.union_band_mask(ref["S"], ref["thr"], hkv) if mode == "union"
+            else A.score_band_mask(ref["S"], ref["thr"]))
+    assert not ((kept_gpu != ref["kept"]) & ~band).any(), label
+    O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), corr)
+    check_blocks(f64(o), O, geo, hkv, lse=f64(lse).T, L=L, label=label)
+    return ref
 
 
 @pytest.mark.parametrize("mode", ["mean", "union"])
@@ -128,17 +139,25 @@ def test_paged_block_sum_cache_chunked_prefill(gpu, mode):
         o1, m1, l1 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True)
         o2, m2, l2 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True, pool_cache=(bsk, bsv, cached))
         torch.cuda.synchronize()
+        # the cached call against the oracle, chunk by chunk
+        off = 0
+        for s in range(2):
+            n = hi[s] - lo[s]
+            _chunk_vs_oracle(pb.seqs[s], lo[s], hi[s], hkv, b, tau, mode, True, o2[off:off + n],
+                             l2[off:off + n], m2[0][s], m2[1][s], f"cached chunk {c} seq {s}")
+            off += n
         assert torch.equal(o1, o2) and torch.equal(l1, l2), f"chunk {c}"
         _same_masks(m1, m2, lo, hi, b)
         cached = (sk // b).to(torch.int32)
-        # the cache now holds every full block of the prefix: compare with the oracle's block sums
+        # the cache now holds every full block of the prefix: the oracle's
+        # block means times the block's key count
         for s in range(2):
-            k = f64(pb.seqs[s]["k"][:hi[s]])
-            v = f64(pb.seqs[s]["v"][:hi[s]])
+            _, kbar, vbar, n_k = A.pool(f64(pb.seqs[s]["q"][:hi[s]]), f64(pb.seqs[s]["k"][:hi[s]]),
+                                        f64(pb.seqs[s]["v"][:hi[s]]), hkv, b)
             for j in range(hi[s] // b):
+                assert n_k[j] == b
                 pg = int(pb.page_table[s, (j * b) // page])
-                ksum = k[j * b:(j + 1) * b].sum(0)          # [Hkv, d]
-                vsum = v[j * b:(j + 1) * b].sum(0)
+                ksum, vsum = kbar[:, j] * n_k[j], vbar[:, j] * n_k[j]      # [Hkv, d]
                 gk = bsk[pg].double().cpu().numpy()
                 gv = bsv[pg].double().cpu().numpy()
                 assert np.abs(gk - ksum).max() <= 1e-5 * np.abs(ksum).max() + 1e-4, (c, s, j)
@@ -150,3 +169,84 @@ def test_paged_block_sum_cache_chunked_prefill(gpu, mode):
     torch.cuda.synchronize()
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
     _same_masks(m1, m3, lo, hi, b)
+
+
+def test_paged_block_sum_cache_without_correction(gpu):
+    """The cached call with the mean correction off and NO value-sum cache
+    (block_sums_v = NULL, which the header allows then): the V means are
+    neither pooled nor cached, and each chunk's masks, outputs and LSE match
+    the oracle without correction, and the uncached call bit for bit."""
+    hq, hkv, d, b, page = 8, 2, 128, 128, 64
+    L = [2048, 1500]
+    bounds = [[0, 700, 1300, 2048], [0, 500, 1000, 1500]]
+    print(f"[case] block-sum cache without correction, NULL V sums, L={L} chunks={bounds}", flush=True)
+    pb = synth.make_paged(15, L, L, hq, hkv, d, b, page_size=page)
+    tau = 0.8
+    p = gpu.make_params(hq, hkv, d, b, tau=tau, mean_correction=False)
+    kc, vc, tab = pb.k_cache.cuda(), pb.v_cache.cuda(), pb.page_table.cuda()
+    bsk, _ = gpu.block_sum_cache(p, kc)
+    cached = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for c in range(3):
+        lo = [bounds[s][c] for s in range(2)]
+        hi = [bounds[s][c + 1] for s in range(2)]
+        q = torch.cat([pb.seqs[s]["q"][lo[s]:hi[s]] for s in range(2)], 0).cuda()
+        cu = torch.tensor([0, hi[0] - lo[0], hi[0] - lo[0] + hi[1] - lo[1]], dtype=torch.int32, device="cuda")
+        sk = torch.tensor(hi, dtype=torch.int32, device="cuda")
+        args = (p, q, cu, sk, max(h - l for h, l in zip(hi, lo)), max(hi), kc, vc, tab)
+        o1, m1, l1 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True)
+        o2, m2, l2 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True, pool_cache=(bsk, None, cached))
+        torch.cuda.synchronize()
+        off = 0
+        for s in range(2):
+            n = hi[s] - lo[s]
+            _chunk_vs_oracle(pb.seqs[s], lo[s], hi[s], hkv, b, tau, "mean", False, o2[off:off + n], l2[off:off + n],
+                             m2[0][s], m2[1][s], f"no-correction cached chunk {c} seq {s}")
+            off += n
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"chunk {c}"
+        _same_masks(m1, m2, lo, hi, b)
+        cached = (sk // b).to(torch.int32)
+
+
+@pytest.mark.parametrize("bad", ["past_end", "negative"])
+def test_validate_rejects_bad_page_id_before_any_kernel(gpu, monkeypatch, bad):
+    """FP2_VALIDATE=1: the paged call copies the lengths and the page table to
+    the host and rejects a page id outside [0, num_pages) with FP2_EINVAL
+    before anything is enqueued (the output buffer keeps its sentinel).  The
+    same call on the valid table passes validation and equals the call
+    without it.  (The invalid table is only ever passed with validation on.)"""
+    monkeypatch.setenv("FP2_VALIDATE", "1")
+    hq, hkv, d, b, page = 8, 2, 128, 128, 64
+    kv_lens, q_lens = [700, 1500], [700, 300]
+    print(f"[case] FP2_VALIDATE bad page id ({bad}) kv_lens={kv_lens}", flush=True)
+    pb = synth.make_paged(16, kv_lens, q_lens, hq, hkv, d, b, page_size=page)
+    p = gpu.make_params(hq, hkv, d, b, tau=0.8)
+    q, cu, sk = pb.q.cuda(), pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda()
+    kc, vc = pb.k_cache.cuda(), pb.v_cache.cuda()
+    tab_ok = pb.page_table.cuda()
+    ref = gpu.sparse_prefill_paged(p, q, cu, sk, max(q_lens), max(kv_lens), kc, vc, tab_ok)
+    torch.cuda.synchronize()
+    n, msq, msk = len(kv_lens), max(q_lens), max(kv_lens)
+    ws = torch.empty(gpu.fp2_paged_workspace_size(p, n, msq, msk), dtype=torch.uint8, device="cuda")
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def call(tab, out):
+        return gpu.fp2_sparse_prefill_paged(p, n, q.data_ptr(), cu.data_ptr(), sk.data_ptr(), msq, msk, kc.data_ptr(),
+                                            vc.data_ptr(), kc.shape[0], kc.shape[1], tab.data_ptr(), tab.shape[1],
+                                            out.data_ptr(), None, None, None, ws.data_ptr(), ws.numel(), sh)
+
+    # valid table under validation: same result as without it
+    out = torch.full_like(ref, 7.0)
+    assert call(tab_ok, out) == gpu.FP2_OK, gpu.last_error()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    # one page id of sequence 1 (inside its seqlens_k) out of range
+    tab = pb.page_table.clone()
+    tab[1, 10] = kc.shape[0] if bad == "past_end" else -3
+    tab_bad = tab.cuda()
+    out = torch.full_like(ref, 7.0)
+    st = call(tab_bad, out)
+    msg = gpu.last_error()
+    torch.cuda.synchronize()
+    print(f"[validate] status {gpu.status_string(st)}: {msg}", flush=True)
+    assert st == gpu.FP2_EINVAL and "page id" in msg
+    assert bool((out == 7.0).all()), "a kernel ran after the validation error"

@@ -251,6 +251,64 @@ def test_select_union_reductions():
     assert A.sparsity(ki, ids) == 0.0
 
 
+def test_score_band_mask_hand_cases():
+    """The band is |S - thr| <= band per (head, row), NaN (invisible) entries
+    outside it.  Values are exact binary fractions, so the <= edge is exact;
+    the two heads and two rows have different thresholds, so a transposed or
+    mis-broadcast threshold fails."""
+    t = 2.0 ** -10                                   # 0.0009765625 < 1e-3 < 2^-9
+    S = np.array([[[0.5, 0.5 + t, 0.5 - t, 0.5 + 2 * t],      # head 0, row 0: thr 0.5
+                   [1.0, 0.25, 0.25 - t, np.nan]],            # head 0, row 1: thr 0.25
+                  [[-1.0, -1.0 - t, 0.5, -1.0 + 4 * t],       # head 1, row 0: thr -1
+                   [3.0, 3.0 + t, 2.0, np.nan]]])             # head 1, row 1: thr 3
+    thr = np.array([[0.5, 0.25], [-1.0, 3.0]])
+    want = np.array([[[True, True, True, False],
+                      [False, True, True, False]],
+                     [[True, True, False, False],
+                      [True, True, False, False]]])
+    assert np.array_equal(A.score_band_mask(S, thr), want)
+    # a wider band takes in the 2t and 4t entries, never the NaN ones
+    want2 = want.copy()
+    want2[0, 0, 3] = want2[1, 0, 3] = True
+    assert np.array_equal(A.score_band_mask(S, thr, band=4 * t), want2)
+    # band 0: exactly the entries equal to their threshold
+    assert np.array_equal(A.score_band_mask(S, thr, band=0.0), S == thr[:, :, None])
+
+
+def test_union_band_mask_hand_cases():
+    """A group's block is in the band when ANY query head of the group
+    (heads h*G .. h*G+G-1) scores it within the band of that head's own
+    threshold.  Four query heads, two groups: the in-band entries are placed
+    so that grouping heads by hq % Hkv instead of hq // G, or using another
+    head's threshold, gives a different answer."""
+    t = 2.0 ** -10
+    Hq, Hkv, nqb, nkb = 4, 2, 1, 4
+    thr = np.array([[0.0], [1.0], [2.0], [3.0]])     # per query head, one row
+    S = np.full((Hq, nqb, nkb), 10.0)                # far from every threshold
+    S[0, 0, 0] = 0.0 + t                             # head 0 (group 0) in band at block 0
+    S[1, 0, 1] = 1.0 - t                             # head 1 (group 0) in band at block 1
+    S[2, 0, 2] = 2.0                                 # head 2 (group 1) in band at block 2
+    S[3, 0, 3] = 0.0                                 # head 3: within band of head 0's threshold only
+    S[3, 0, 1] = np.nan                              # invisible entry: never in band
+    want = np.zeros((Hkv, nqb, nkb), dtype=bool)
+    want[0, 0, [0, 1]] = True
+    want[1, 0, 2] = True
+    got = A.union_band_mask(S, thr, Hkv)
+    assert got.shape == (Hkv, nqb, nkb)
+    assert np.array_equal(got, want)
+    # explicit loop over groups and heads
+    loop = np.zeros_like(want)
+    G = Hq // Hkv
+    for h in range(Hkv):
+        for g in range(G):
+            hq = h * G + g
+            for j in range(nkb):
+                x = S[hq, 0, j]
+                if not np.isnan(x) and abs(x - thr[hq, 0]) <= 1e-3:
+                    loop[h, 0, j] = True
+    assert np.array_equal(got, loop)
+
+
 def test_sparsity_definition():
     kept = np.zeros((1, 4, 4), dtype=bool)
     kept[0, np.arange(4), np.arange(4)] = True    # 4 kept of 1+2+3+4 = 10 visible
