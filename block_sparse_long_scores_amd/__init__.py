@@ -66,6 +66,7 @@ _SIGS = {
     "fp2_max_seqlen_k": (_i32, [_P]),
     "fp2_select_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "fp2_select_blocks": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fp2_select_blocks_noalloc": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp2_sparse_prefill": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp2_dense_prefill": (ctypes.c_int, [_P, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "fp2_paged_mask_dims": (None, [_P, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
@@ -131,6 +132,12 @@ def fp2_select_blocks(params, batch, seqlen_q, seqlen_k, q, k, v, block_idx, blo
                       workspace, workspace_bytes, stream):
     return load().fp2_select_blocks(ctypes.byref(params), batch, seqlen_q, seqlen_k, q, k, v, block_idx, block_cnt,
                                     pooled_k, pooled_v, workspace, workspace_bytes, stream)
+
+
+def fp2_select_blocks_noalloc(params, batch, seqlen_q, seqlen_k, q, k, v, block_idx, block_cnt, pooled_k, pooled_v,
+                              stream):
+    return load().fp2_select_blocks_noalloc(ctypes.byref(params), batch, seqlen_q, seqlen_k, q, k, v, block_idx,
+                                            block_cnt, pooled_k, pooled_v, stream)
 
 
 def fp2_sparse_prefill(params, batch, seqlen_q, seqlen_k, q, k, v, block_idx, block_cnt, pooled_k, pooled_v, out,

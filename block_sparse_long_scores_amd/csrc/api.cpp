@@ -134,6 +134,10 @@ void fill_attn_common(AttnArgs& a, const fp2_params* p) {
 
 }  // namespace
 
+namespace fp2 {
+int set_last_error(int st, const char* msg) { return fail((fp2_status)st, "%s", msg); }
+}  // namespace fp2
+
 extern "C" {
 
 int32_t fp2_num_q_blocks(int32_t seqlen_q, int32_t seqlen_k, int32_t block_size) {

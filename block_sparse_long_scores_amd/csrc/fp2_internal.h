@@ -121,4 +121,8 @@ hipError_t launch_attention_fp8(const AttnArgs& a, int D, int block, hipStream_t
 size_t attention_lds_bytes_bf16(int D, int block, int nkb);
 size_t attention_lds_bytes_fp8(int D, int block, int nkb);
 
+// Records msg as the calling thread's last error (fp2_last_error) and
+// returns st; for entry points defined outside api.cpp.
+int set_last_error(int st, const char* msg);
+
 }  // namespace fp2

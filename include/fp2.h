@@ -158,6 +158,28 @@ fp2_status fp2_select_blocks(const fp2_params* p, int32_t batch,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* fp2_select_blocks without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing: the pooled query
+ * blocks go to a static 16 MiB device array of the library (one copy per
+ * GPU, held until the process ends).  Same arguments, kernels and results as
+ * fp2_select_blocks.
+ *   Limit: fp2_select_workspace_size(p, batch, seqlen_q, seqlen_k) must be at
+ *   most 16 MiB (16777216 bytes), e.g. batch 4 at 128K tokens with 8 KV
+ *   heads, d = 128, group-mean selection; larger calls return
+ *   FP2_EUNSUPPORTED before anything is enqueued.  Other errors as
+ *   fp2_select_blocks; FP2_EDEVICE if the array's device address cannot be
+ *   obtained on the current device.
+ *   All calls on one GPU share the array: calls that overlap in time on one
+ *   GPU (different streams, or a captured graph replayed next to another
+ *   call) race and give undefined results.  Calls in stream order are safe. */
+fp2_status fp2_select_blocks_noalloc(const fp2_params* p, int32_t batch,
+                                     int32_t seqlen_q, int32_t seqlen_k,
+                                     const void* q, const void* k, const void* v,
+                                     int32_t* block_idx, int32_t* block_cnt,
+                                     float* pooled_k, float* pooled_v,
+                                     void* stream);
+
 /* Block-sparse causal attention with mean correction (steps 3-5; explainer
  * §2.1 Out_q^V2, §2.2 PackGQA).  Takes the mask and pooled blocks in the
  * layout fp2_select_blocks produces.  Any mask is accepted whose rows are
