@@ -59,6 +59,12 @@ constexpr int NT = kRowsPerWave / 32;  // 32-query column groups per wave
 constexpr float kRefMargin = 16.0f;     // log2 units above the sink-chunk max
 constexpr float kRefOverflow = 100.0f;  // log2 of the normaliser that forces a rerun
 constexpr int kMaxPasses = 4;
+// fp8 P codes: the e4m3 code of 2^x is taken as RNE(8 (x + 7) - kCodeShift),
+// the exponent-and-mantissa bits read as one fixed-point number of x + 7
+// (a log-linear, Mitchell-style approximation of 2^x: the mantissa is
+// linear in the fraction of x).  The shift centres its error: the decoded
+// code is within a factor exp(+-0.0728) of 2^x over the normal range.
+constexpr float kCodeShift = 0.34f;
 
 template <int D, int BLK, bool F8>
 struct Cfg {
@@ -121,15 +127,19 @@ __device__ __forceinline__ f32x16 qk8_chain(const i32x8 (&k)[1], const i32x8 (&q
 
 // The same chain split into one asm statement per MFMA, so that the
 // compiler can issue independent VALU work between them: the first writes
-// S (C = 0), the last accumulates into it and carries the 20 wait states
-// after which the VALU may read S.  Nothing may touch S between the two
-// (the second MFMA reads it as its exactly overlapping accumulator, which
-// needs no wait states).
+// S (C = 0), the last accumulates into it.  Nothing may touch S between the
+// two (the second MFMA reads it as its exactly overlapping accumulator,
+// which needs no wait states).
 __device__ __forceinline__ void qk8_first(f32x16& S, const i32x8& k, const i32x8& q) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(S) : "v"(k), "v"(q));
 }
+// The last MFMA of a chain in the pipelined stages, whose S the VALU first
+// reads at least 14 instructions later (the rest of the stage's last slot,
+// the next stage's operand reads, and a slot with an MFMA and a max-tree
+// piece): the 8 wait states here make up the 19 that a 16-pass MFMA result
+// needs before a VALU read.
 __device__ __forceinline__ void qk8_last(f32x16& S, const i32x8& k, const i32x8& q) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3"
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\ts_nop 7"
                : "+v"(S)
                : "v"(k), "v"(q));
 }
@@ -264,6 +274,14 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   f32x16 O[C::MT][NT];
   f32x16 Lacc[F8 ? NT : 1];  // fp8: row sums of P, accumulated by MFMA
   float mref[NT], lsum[NT];
+  // fp8: 8 * logit scale; 56 - kCodeShift - 8 * mref (the code offset of
+  // the pass's reference); the largest superchunk maximum above mref seen
+  // in the pass (log2 units), which sets the exact reference of a rerun
+  float cs8[F8 ? NT : 1], base8[F8 ? NT : 1], rmax[F8 ? NT : 1];
+  if constexpr (F8) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) cs8[nt] = 8.f * cs[nt];
+  }
 
   // LDS: K tiles at [0, 2*TILE), V tiles at [2*TILE, 4*TILE) (double buffer)
   char* const lds = smem;
@@ -629,25 +647,41 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       return;
     }
     const float m = max_partner32(maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), mh));
-    float fx = floorf(__builtin_fmaf(m, cs[nt], -mref[nt]));
+    const float rel = __builtin_fmaf(m, cs[nt], -mref[nt]);
+    rmax[nt] = fmaxf(rmax[nt], rel);
+    float fx = floorf(rel);
     fx = fminf(fmaxf(fx, -110.f), 120.f);
     bq = (int)fx - 7;
-    bias = mref[nt] + (float)bq;
+    bias = __builtin_fmaf(-8.f, (float)bq, base8[nt]);  // code offset: 8 (7 - mref - bq) - kCodeShift
   };
+  // The e4m3 code of P = 2^x, x = S cs - mref - bq, is the saturating
+  // round-to-nearest byte of 8 (x + 7) - kCodeShift = S cs8 + bias: one FMA
+  // and one convert per score, no exponential (a superchunk's largest x is
+  // below 8, so the largest code is 0x78 = 256; masked scores give 0).
   auto sm8_exp = [&](const f32x16 (&Sn)[2], int q, int j, int nt, const float bias, i32x8& pk)
       __attribute__((always_inline)) {
-    const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 0], cs[nt], -bias));
-    const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 1], cs[nt], -bias));
-    const float x2 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 2], cs[nt], -bias));
-    const float x3 = __builtin_amdgcn_exp2f(__builtin_fmaf(Sn[q][4 * j + 3], cs[nt], -bias));
-    // (the first convert's other half is overwritten by the second: x0's
-    // own register serves as its old value, no zeroing move)
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
-    pk[4 * q + j] = w;
+    const float y0 = __builtin_fmaf(Sn[q][4 * j + 0], cs8[nt], bias);
+    const float y1 = __builtin_fmaf(Sn[q][4 * j + 1], cs8[nt], bias);
+    const float y2 = __builtin_fmaf(Sn[q][4 * j + 2], cs8[nt], bias);
+    const float y3 = __builtin_fmaf(Sn[q][4 * j + 3], cs8[nt], bias);
+    // (every byte is written: y0's own register serves as the old value)
+    unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(y0, 0, __float_as_uint(y0));
+    w = __builtin_amdgcn_cvt_pk_u8_f32(y1, 1, w);
+    w = __builtin_amdgcn_cvt_pk_u8_f32(y2, 2, w);
+    w = __builtin_amdgcn_cvt_pk_u8_f32(y3, 3, w);
+    pk[4 * q + j] = (int)w;
   };
-  const i32x8 ones8 = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                            0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // e4m3 1.0 in every byte: the A operand of the row-sum MFMA.  Defined by
+  // vector moves so that it lives in vector registers (as a uniform constant
+  // the compiler keeps it in scalar registers, spills those, and rebuilds the
+  // operand with 12 lane reads and moves at every use).
+  i32x8 ones8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    int one;
+    asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one));
+    ones8[e] = one;
+  }
   auto pv8 = [&](const i32x8 (&vop)[C::MT], const i32x8& pk, int sbyte, int nt) __attribute__((always_inline)) {
     if constexpr (F8) {
 #pragma unroll
@@ -813,7 +847,11 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) O[mt][nt] = f32x16{};
       lsum[nt] = 0.f;
-      if constexpr (F8) Lacc[nt] = f32x16{};
+      if constexpr (F8) {
+        Lacc[nt] = f32x16{};
+        base8[nt] = (56.f - kCodeShift) - 8.f * mref[nt];
+        rmax[nt] = -INFINITY;
+      }
     }
     if constexpr (F8 && CARRY8) {  // the carried P V of the pass's first block adds nothing
 #pragma unroll
@@ -976,11 +1014,17 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     // A row whose normaliser overflowed the range reruns the tile with its
     // reference moved up (all rows of the workgroup take part in the rerun;
     // rows that were fine recompute the same values).
+    // fp8: a superchunk maximum more than kRefOverflow above the reference
+    // (its codes may have left e4m3's range) reruns with the reference at
+    // that maximum, which bounds every code of the rerun.
     bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float lt = (F8 ? Lacc[nt][0] : 0.f) + lsum[nt] + partner32(lsum[nt]);
-      if (!(lt < __builtin_exp2f(kRefOverflow))) {
+      if (F8 && rmax[F8 ? nt : 0] > kRefOverflow) {
+        bad = true;
+        mref[nt] += rmax[F8 ? nt : 0];
+      } else if (!(lt < __builtin_exp2f(kRefOverflow))) {
         bad = true;
         mref[nt] += (lt < INFINITY) ? log2f(lt) : kRefOverflow;
       }

@@ -37,7 +37,10 @@ def max_abs(a, b):
 
 
 BF16_LSE_ABS = 2e-2    # LSE tolerance, bf16 path
-FP8_LSE_ABS = 0.07     # LSE tolerance, fp8 path: e4m3 rounding of P, ln(1 + 2^-4) = 0.061
+# LSE tolerance, fp8 path: P is stored as log-linear e4m3 codes, each within a
+# factor exp(+-0.0728) of its exact value (tests/test_tolerances.py), so a row
+# dominated by one key can have its normaliser off by up to 0.0728
+FP8_LSE_ABS = 0.08
 
 
 def block_errors(o, O, geo, hkv, blocks=None, lse=None, L=None):
@@ -65,7 +68,7 @@ def block_errors(o, O, geo, hkv, blocks=None, lse=None, L=None):
 def check_blocks(o, O, geo, hkv, fp8=False, blocks=None, lse=None, L=None, label="parity", rel_tol=None):
     """Hold every (query block, KV head) pair to the output tolerance on its
     own (rel-L2 <= 1e-2 and max-abs <= 2e-2 in bf16, rel-L2 <= 5e-2 in fp8;
-    LSE within 2e-2 / 0.07), so that large outputs of one block (the first
+    LSE within 2e-2 / 0.08), so that large outputs of one block (the first
     query blocks attend to few keys) cannot hide the error of another.
     Prints the worst pair and the last block; returns the error list."""
     errs = block_errors(o, O, geo, hkv, blocks, lse, L)

@@ -16,11 +16,11 @@ from tests.helpers import FP8_LSE_ABS, FP8_REL_L2, assert_mask_matches, check_bl
 
 pytestmark = pytest.mark.gpu
 
-# LSE bound of the fp8 path (FP8_LSE_ABS = 0.07): P is stored in e4m3 (3
-# mantissa bits, round to nearest, relative error <= 2^-4) and the row sums
-# are taken over the stored P, so a row dominated by a single key can have
-# its normaliser off by up to ln(1 + 2^-4) = 0.061 (its output is not
-# affected: numerator and normaliser share the same stored P).
+# LSE bound of the fp8 path (FP8_LSE_ABS = 0.08): P is stored as e4m3 codes
+# read as a log-linear approximation of 2^x (each within a factor exp(+-0.0728)
+# of the exact value) and the row sums are taken over the stored P, so a row
+# dominated by a single key can have its normaliser off by up to 0.0728 (its
+# output is not affected: numerator and normaliser share the same stored P).
 
 
 class Fp8Case:
