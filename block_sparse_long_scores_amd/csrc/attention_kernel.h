@@ -57,8 +57,18 @@ constexpr int kRowsPerWave = 64;
 constexpr int kRowsPerPart = 256;
 constexpr int NT = kRowsPerWave / 32;  // 32-query column groups per wave
 constexpr float kRefMargin = 16.0f;     // log2 units above the sink-chunk max
-constexpr float kRefOverflow = 100.0f;  // log2 of the normaliser that forces a rerun
-constexpr int kMaxPasses = 4;
+constexpr float kRefOverflow = 100.0f;  // log2 units above the reference that force a rerun
+// Passes of a tile (see the rerun rule at the end of attn_tile): a row whose
+// normaliser overflowed is searched for (steps doubling from 128 log2 units,
+// then bisected), which reaches logits up to ~8e6 log2 units above the first
+// reference within 32 passes; a row still unresolved after the last pass is
+// written as NaN.
+constexpr int kMaxPasses = 32;
+constexpr float kFirstStep = 128.0f;
+// A normaliser below 2^-kRefUnder after a step up means the reference
+// overshot: its largest terms sit near fp32's denormal range and lose
+// precision (the first pass's normaliser is at least 2^-kRefMargin).
+constexpr float kRefUnder = 60.0f;
 // fp8 P codes: the e4m3 code of 2^x is taken as RNE(8 (x + 7) - kCodeShift),
 // the exponent-and-mantissa bits read as one fixed-point number of x + 7
 // (a log-linear, Mitchell-style approximation of 2^x: the mantissa is
@@ -275,9 +285,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   f32x16 Lacc[F8 ? NT : 1];  // fp8: row sums of P, accumulated by MFMA
   float mref[NT], lsum[NT];
   // fp8: 8 * logit scale; 56 - kCodeShift - 8 * mref (the code offset of
-  // the pass's reference); the largest superchunk maximum above mref seen
-  // in the pass (log2 units), which sets the exact reference of a rerun
+  // the pass's reference); the largest superchunk maximum above mref (log2
+  // units) seen in the pass, which sets the exact reference of a rerun.
   float cs8[F8 ? NT : 1], base8[F8 ? NT : 1], rmax[F8 ? NT : 1];
+  // rerun search step per row (log2 units; negative once bracketed)
+  float rstep[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rstep[nt] = kFirstStep;
   if constexpr (F8) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) cs8[nt] = 8.f * cs[nt];
@@ -1014,20 +1028,47 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     // A row whose normaliser overflowed the range reruns the tile with its
     // reference moved up (all rows of the workgroup take part in the rerun;
     // rows that were fine recompute the same values).
-    // fp8: a superchunk maximum more than kRefOverflow above the reference
-    // (its codes may have left e4m3's range) reruns with the reference at
-    // that maximum, which bounds every code of the rerun.
+    // Rerun rule, per row (both lane halves of a query column see the same
+    // normaliser lt and take the same decision):
+    //  * fp8: a superchunk maximum more than kRefOverflow above the reference
+    //    (its codes may have left e4m3's range): the reference moves up to
+    //    that maximum, after which every code of the rerun is in range;
+    //  * a finite normaliser of 2^kRefOverflow or more: the reference moves up
+    //    by log2(lt), which is at least the largest exponent, so every term
+    //    of the rerun is at most 1;
+    //  * an overflowed normaliser (some exponent beyond fp32's range): the
+    //    reference moves up by a step that doubles from kFirstStep until a
+    //    pass's normaliser falls below 2^-kRefUnder (the reference overshot)
+    //    and is bisected from then on; the window of references that give a
+    //    normaliser in [2^-kRefUnder, 2^kRefOverflow) is 160 log2 units wide,
+    //    so the search ends there with every term at full precision.
+    // All rows of the workgroup rerun; rows that were fine recompute the
+    // same values.  A row still unresolved after the last pass is written
+    // as NaN (its logits exceed the first reference by more than ~8e6).
     bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float lt = (F8 ? Lacc[nt][0] : 0.f) + lsum[nt] + partner32(lsum[nt]);
+      const float st = rstep[nt];
+      bool bad_nt = false;
       if (F8 && rmax[F8 ? nt : 0] > kRefOverflow) {
-        bad = true;
+        bad_nt = true;
         mref[nt] += rmax[F8 ? nt : 0];
-      } else if (!(lt < __builtin_exp2f(kRefOverflow))) {
-        bad = true;
-        mref[nt] += (lt < INFINITY) ? log2f(lt) : kRefOverflow;
+      } else if (lt >= __builtin_exp2f(kRefOverflow) && lt < INFINITY) {
+        bad_nt = true;
+        mref[nt] += log2f(lt);
+      } else if (lt == INFINITY) {  // overflow: step up
+        bad_nt = true;
+        mref[nt] += fabsf(st) * (st < 0.f ? 0.5f : 1.f);
+        rstep[nt] = st < 0.f ? 0.5f * st : 2.f * st;
+      } else if (lt < __builtin_exp2f(-kRefUnder) && st != kFirstStep) {  // overshot a step up: bisect back
+        bad_nt = true;
+        const float half = st < 0.f ? -0.5f * st : 0.25f * st;
+        mref[nt] -= half;
+        rstep[nt] = -half;
       }
+      if (bad_nt && pass + 1 == kMaxPasses) lsum[nt] = __builtin_nanf("");  // unresolved row: NaN
+      bad |= bad_nt;
     }
     if (!__syncthreads_or(bad)) break;
   }

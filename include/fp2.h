@@ -49,6 +49,16 @@
  *    call returns a negative fp2_status, enqueues nothing, and
  *    fp2_last_error() (thread-local) describes the problem.  A failed launch
  *    returns FP2_EDEVICE.  No C++ exception crosses this interface.
+ *  - Numerical range: each query row's softmax runs against a fixed
+ *    reference (the largest logit over the first 32 keys of the row's first
+ *    kept block, plus a margin) instead of a running maximum.  A row whose
+ *    normaliser leaves fp32's range against it (logits far above that
+ *    reference) makes its workgroup recompute the tile with the reference
+ *    moved up (to the pass's normaliser, its largest fp8 superchunk maximum,
+ *    or found by a doubling-then-bisecting search when the normaliser
+ *    overflowed), so results are those of the exact softmax for logits up
+ *    to 4e6 log2 units above the reference; a row beyond that is written as
+ *    NaN (and its lse as NaN).  Logits must be finite in fp32.
  *  - Supported shapes: head_dim in {64, 128}; block_size in {64, 128};
  *    num_q_heads a positive multiple of num_kv_heads, with num_q_heads *
  *    head_dim <= 8192 and num_kv_heads * head_dim <= 4096 for bf16 inputs

@@ -113,19 +113,22 @@ def test_fp8_tau_inf_sparse_equals_dense(gpu):
     assert torch.equal(out_s, out_d)
 
 
+@pytest.mark.parametrize("shift", [200.0, 800.0, 8000.0])
 @pytest.mark.parametrize("fp8", [True, False])
-def test_large_logits_rerun(gpu, fp8):
-    """A block of keys whose logits exceed the sink block's by ~150 (log2):
-    the normaliser overflows fp32 against the first reference, so the tile
-    reruns with the reference moved up; fp8 also exercises the per-chunk P
-    scaling over that range."""
+def test_large_logits_rerun(gpu, fp8, shift):
+    """A block of keys whose logits exceed the sink block's by ~150, ~600 and
+    ~6100 (log2 units): the first pass's reference (the sink chunk's maximum)
+    is far below the row maximum, so the tile reruns with its reference at
+    the largest exponent the first pass saw, which is exact for any finite
+    logits; fp8 also exercises the per-superchunk P scaling over that range."""
     hq, hkv, d, b, S = 4, 1, 128, 128, 1024
+    print(f"[case] large logits fp8={fp8} shift={shift}", flush=True)
     pr = synth.make_problem("iid", 25, S, hq, hkv, d, b)
     q = pr.q.float()
     k = pr.k.float()
     u = torch.ones(d) / math.sqrt(d)
     q += 6.0 * u                     # every query aligns with u
-    k[600:700] += 200.0 * u          # logits ~ 6 * 200 / sqrt(d) ~ 106 nats above the rest
+    k[600:700] += shift * u          # logits ~ 6 * shift / sqrt(d) nats above the rest
     q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
     if fp8:
         qc, qs = synth.quantize_e4m3(q, 1)
@@ -145,10 +148,11 @@ def test_large_logits_rerun(gpu, fp8):
     out, lse = gpu.dense_prefill(p, *args, return_lse=True)
     torch.cuda.synchronize()
     O, L = A.dense_attention(qn, kn, vn, hkv, 1 / math.sqrt(d))
-    print(f"[rerun fp8={fp8}] lse range {L.min():.1f}..{L.max():.1f}", flush=True)
-    assert L.max() - L.min() > 60
+    print(f"[rerun fp8={fp8} shift={shift}] lse range {L.min():.1f}..{L.max():.1f} nats "
+          f"({(L.max() - L.min()) / math.log(2):.0f} log2 units)", flush=True)
+    assert L.max() - L.min() > 0.3 * shift
     check_blocks(out.double().cpu().numpy(), O, A.geometry(S, S, b), hkv, fp8=fp8,
-                 lse=lse[0].double().cpu().numpy(), L=L, label=f"rerun fp8={fp8}", rel_tol=tol)
+                 lse=lse[0].double().cpu().numpy(), L=L, label=f"rerun fp8={fp8} shift={shift}", rel_tol=tol)
 
 
 # 64-row pages take the per-tile copy-offset table, 32-row pages (which do
