@@ -300,7 +300,7 @@ void fp2_paged_mask_dims(const fp2_params* p, int32_t max_seqlen_q, int32_t max_
 
 namespace {
 struct PagedLayout {
-  size_t qbar, kbar, vbar, idx, cnt, plan, total;
+  size_t qbar, kbar, vbar, idx, cnt, plan, sched, total;
 };
 PagedLayout paged_layout(const fp2_params* p, int n, int max_nqb, int max_nkb) {
   PagedLayout L{};
@@ -319,6 +319,8 @@ PagedLayout paged_layout(const fp2_params* p, int n, int max_nqb, int max_nkb) {
   off += align_up((size_t)n * H * max_nqb * 4);
   L.plan = off;  // task count, then the work-ordered task list
   off += align_up(16 + (size_t)n * H * max_nqb * 4);
+  L.sched = off;  // the attention launch's 8 tile-queue counters, 128 bytes apart
+  off += align_up(8 * 128);
   L.total = off;
   return L;
 }
@@ -438,6 +440,7 @@ static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* 
   pl.block_cnt = cnt;
   pl.plan_count = (int32_t*)(ws + L.plan);
   pl.plan = (int32_t*)(ws + L.plan + 16);
+  pl.sched = (unsigned*)(ws + L.sched);
   pl.Hkv = p->num_kv_heads;
   pl.block = b;
   pl.mean_correction = p->mean_correction;
@@ -447,6 +450,7 @@ static fp2_status paged_impl(const fp2_params* p, int32_t num_seqs, const void* 
   fill_attn_common(a, p);
   a.plan = pl.plan;
   a.plan_count = pl.plan_count;
+  a.sched = pl.sched;
   a.seq = sd;
   a.kv = kv;
   a.q = q;

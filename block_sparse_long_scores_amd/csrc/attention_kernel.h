@@ -48,7 +48,10 @@
 #include "geometry.h"
 
 #include <atomic>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 namespace fp2 {
 namespace {  // internal: every precision's translation unit has its own copy
@@ -1137,12 +1140,20 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
 // queues in turn once its own is drained.  Workgroups never wait for the
 // hardware dispatcher between tiles (with tiles of very different lengths that
 // dispatcher leaves CUs idle), while the two parts of one tile and the tiles
-// of one head in a query-block rank stay in one XCD's L2.  g_sched holds one
-// set of 8 counters (each on its own 128-byte line) per launch slot; the
-// launcher zeroes the slot's counters with sched_reset_kernel on the same
-// stream right before the launch, and hands out slots round-robin so that
-// launches running concurrently on different streams use different counters.
-constexpr int kSchedSlots = 64;
+// of one head in a query-block rank stay in one XCD's L2.
+//
+// The 8 counters (each on its own 128-byte line) must be zero when the
+// launch starts and must belong to no launch that can run at the same time.
+// Paged launches keep them in the caller's workspace (zeroed by the plan
+// kernel before them on the stream).  Contiguous launches, which take no
+// workspace, use one of the sets in g_sched, zeroed by sched_reset_kernel on
+// the launch's stream right before it: the first kStreamSlots streams a
+// process launches on each get a set of their own (a stream's launches run
+// in order, so they can share it), and a launch captured into a HIP graph
+// takes the next of kCaptureSlots further sets, which no eager launch uses.
+constexpr int kStreamSlots = 192;
+constexpr int kCaptureSlots = 64;
+constexpr int kSchedSlots = kStreamSlots + kCaptureSlots;
 __device__ unsigned int g_sched[kSchedSlots][8][32];
 
 __global__ void sched_reset_kernel(int slot) {
@@ -1155,7 +1166,7 @@ void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int nwg = gridDim.x;
   const int home = blockIdx.x & 7;
-  unsigned int(*ctr)[32] = g_sched[a.sched_slot];
+  unsigned int(*ctr)[32] = a.sched ? (unsigned int(*)[32])a.sched : g_sched[a.sched_slot];
   // tiles in queue q: all positions below it are tiles
   const int ntask = a.plan ? __builtin_amdgcn_readfirstlane(a.plan_count[0]) : a.ntiles;
   auto queue_len = [&](int q) -> int {
@@ -1237,37 +1248,78 @@ static int compute_units() {
   return n;
 }
 
-static std::atomic<unsigned> g_slot_counter{0};
+// The library's counter set for a contiguous launch on stream st (see the
+// scheduler above): a captured launch takes the next capture set in turn;
+// otherwise the stream keeps the set it got at its first launch on this
+// device, sets being handed out in first-use order (past kStreamSlots
+// streams the oldest assignment is taken over).
+static int sched_slot_for(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t ce = hipStreamIsCapturing(st, &cs);
+  if (ce == hipSuccess && cs == hipStreamCaptureStatusActive) {
+    static std::atomic<unsigned> next_capture{0};
+    return kStreamSlots + (int)(next_capture.fetch_add(1) % kCaptureSlots);
+  }
+  if (ce != hipSuccess) (void)hipGetLastError();  // a refused capture query leaves no error behind
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, int> slot_of;
+  static std::pair<int, hipStream_t> owner[64][kStreamSlots];
+  static int next[64];
+  const int dv = dev & 63;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, st);
+  const auto it = slot_of.find(key);
+  if (it != slot_of.end()) return it->second;
+  const int slot = next[dv]++ % kStreamSlots;
+  if (next[dv] > kStreamSlots) slot_of.erase(owner[dv][slot]);
+  owner[dv][slot] = key;
+  slot_of[key] = slot;
+  return slot;
+}
 
 template <int D, int BLK, bool F8>
 static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
   if (attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride) > 160 * 1024) return hipErrorInvalidValue;
   if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
-  // 1: the kernel's static segment fits the allowance; -1: it does not
+  // once per kernel: the static segment fits the allowance (1) or not (-1),
+  // and the dynamic-LDS limit is raised to everything the allowance leaves
+  // (launches then pass their own size, which never lowers the limit)
   static std::atomic<int> static_ok{0};
-  int ok = static_ok.load(std::memory_order_relaxed);
+  static std::mutex init_mu;
+  int ok = static_ok.load(std::memory_order_acquire);
   if (ok == 0) {
-    hipFuncAttributes fa;
-    if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8>) != hipSuccess) return hipErrorInvalidValue;
-    ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
-    static_ok.store(ok, std::memory_order_relaxed);
+    std::lock_guard<std::mutex> lock(init_mu);
+    ok = static_ok.load(std::memory_order_relaxed);
+    if (ok == 0) {
+      hipFuncAttributes fa;
+      if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8>) != hipSuccess) return hipErrorInvalidValue;
+      ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
+      if (ok > 0) {
+        const hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 160 * 1024 - kStaticLdsBytes);
+        if (e != hipSuccess) return e;
+      }
+      static_ok.store(ok, std::memory_order_release);
+    }
   }
   if (ok < 0) return hipErrorInvalidValue;
   const size_t lds_total = attn_dyn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
-  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_total);
-  if (e != hipSuccess) return e;
   if (ntiles == 0) return hipSuccess;
   AttnArgs a = a0;
   a.ntiles = (int)ntiles;
-  a.sched_slot = (int)(g_slot_counter.fetch_add(1) % kSchedSlots);
   a.lds_dtab = (int)attn_lds_dtab<D, BLK, F8>(a0.seq.nkb_stride);
   a.lds_sched = (int)(lds_total - kSchedLdsBytes);
   const long grid = ntiles < compute_units() ? ntiles : compute_units();
-  hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, st, a.sched_slot);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.sched) {
+    a.sched_slot = sched_slot_for(st);
+    hipLaunchKernelGGL(sched_reset_kernel, dim3(1), dim3(64), 0, st, a.sched_slot);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_kernel<D, BLK, F8>), dim3((unsigned)grid), dim3(64 * a.waves), lds_total, st, a);
   return hipGetLastError();
 }

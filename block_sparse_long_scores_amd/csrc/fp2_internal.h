@@ -75,6 +75,7 @@ struct PlanArgs {
   const int* block_cnt;     // [B, Hkv, nqb_stride]
   int* plan;                // out: task ids (s*Hkv + h)*nqb_stride + il, longest first
   int* plan_count;          // out: number of tasks
+  unsigned* sched;          // out: the attention launch's tile-queue counters, zeroed
   int Hkv, block, mean_correction;
 };
 
@@ -103,9 +104,12 @@ struct AttnArgs {
   int nqb_grid;             // query-block extent of the tile space
   const int* plan;          // optional work-ordered task list (PlanArgs) or nullptr
   const int* plan_count;
+  // tile-queue counters (8 x 32 unsigned, zeroed before the launch) in caller
+  // memory, or nullptr: the launcher then takes one of the library's sets
+  unsigned* sched;
   // set by the launcher
   int ntiles;               // Hkv * batch * parts * nqb_grid
-  int sched_slot;           // tile-scheduler counter slot of this launch
+  int sched_slot;           // the library's counter set used when sched is nullptr
   int lds_sched;            // LDS byte offset of the next-tile broadcast
   int lds_dtab;             // LDS byte offset of the copy-offset table
 };

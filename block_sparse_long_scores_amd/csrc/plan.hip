@@ -9,7 +9,8 @@
 // the tasks by an estimate of their work, in 32-key chunks: kept blocks x
 // (block / 32) + dropped blocks / 32 (the mean-correction pseudo-keys) + 2
 // (the fixed cost of a tile).  Ties keep no particular order; the outputs do
-// not depend on the order.
+// not depend on the order.  The kernel also zeroes the attention launch's
+// tile-queue counters, which live in the same caller workspace.
 #include "fp2_device.h"
 #include "fp2_internal.h"
 #include "geometry.h"
@@ -26,6 +27,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int per_seq = a.Hkv * a.seq.nqb_stride;
   const int ntask_all = a.seq.batch * per_seq;
   for (int b = tid; b < kPlanBins; b += kPlanThreads) hist[b] = 0;
+  // the attention launch that follows on the same stream starts its tile
+  // queues from these counters (each on its own 128-byte line)
+  if (tid < 8) a.sched[32 * tid] = 0u;
   __syncthreads();
 
   // work estimate of task t (-1: no query block there)

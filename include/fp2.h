@@ -36,11 +36,18 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    default stream).  Buffers must stay valid until the stream has run it.
  *    Only kernels are enqueued (no memset, copy or host synchronisation), so
- *    a call can be captured into a HIP graph.  Each attention launch takes
- *    one of 64 device-side tile-queue counter sets in turn, which its own
- *    first kernel clears: up to 64 launches may run at once on different
- *    streams, and a captured launch keeps its set, so one graph must not be
- *    replayed on two streams at the same time.
+ *    a call can be captured into a HIP graph.  The attention kernel pulls
+ *    its tiles from 8 device-side counters that no concurrent launch may
+ *    share.  The paged entry points keep them in the caller's workspace.
+ *    fp2_sparse_prefill and fp2_dense_prefill use one of the library's sets:
+ *    each of the first 192 streams a process launches them on gets a set of
+ *    its own (reused by that stream's later launches, which run in order;
+ *    beyond 192 streams the oldest stream's set is handed on), and a launch
+ *    captured into a HIP graph gets the next of 64 further sets, which no
+ *    eager launch uses.  So launches on different streams may run at once,
+ *    and graph replays may run next to eager launches on any stream; one
+ *    graph must not be replayed concurrently with itself, or with a graph
+ *    whose launch was captured a multiple of 64 captured launches later.
  *  - Layouts are row-major.  Contiguous tensors are BSHD: q [B, Sq, Hq, d],
  *    k and v [B, Sk, Hkv, d], out [B, Sq, Hq, d].  Query head hq reads KV
  *    head hq / G.  Query row r of a sequence sits at absolute position

@@ -108,3 +108,47 @@ def test_two_streams_at_once(gpu):
         for i in (0, 1):
             assert torch.equal(outs[i], ref[i]), (rep, i)
     print("[streams] concurrent launches equal the sequential ones", flush=True)
+
+
+def test_graph_replays_next_to_many_eager_launches(gpu):
+    """A captured attention launch replayed on one stream while another
+    stream runs 70 eager attention launches (more than the 64 capture sets
+    of tile-queue counters) with no synchronisation in between: the
+    capture keeps a counter set that no eager launch takes, and the eager
+    stream reuses its own, so every replay and every eager launch equals its
+    sequential result."""
+    hq, hkv, d, b = 8, 2, 128, 128
+    print("[case] graph replay next to 70 eager launches on another stream", flush=True)
+    q1, k1, v1 = _problem(25)
+    q2, k2, v2 = _problem(26, S=2000)
+    p = gpu.make_params(hq, hkv, d, b, tau=0.8)
+    sel1 = gpu.select_blocks(p, q1, k1, v1)
+    sel2 = gpu.select_blocks(p, q2, k2, v2)
+    ref1 = gpu.sparse_prefill(p, q1, k1, v1, *sel1)
+    ref2 = gpu.sparse_prefill(p, q2, k2, v2, *sel2)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    sa.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(sa):
+        gpu.sparse_prefill(p, q1, k1, v1, *sel1)     # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=sa):
+        out1 = gpu.sparse_prefill(p, q1, k1, v1, *sel1)
+    outs2 = [torch.empty_like(ref2) for _ in range(70)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out1.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            g.replay()
+        with torch.cuda.stream(sb):
+            for o in outs2:
+                gpu.sparse_prefill(p, q2, k2, v2, *sel2, out=o)
+        with torch.cuda.stream(sa):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out1, ref1), rep
+        for i, o in enumerate(outs2):
+            assert torch.equal(o, ref2), (rep, i)
+    print("[graph] replays and 210 concurrent eager launches equal their sequential results", flush=True)
