@@ -82,6 +82,25 @@ def blas_info():
     return "unknown", os.cpu_count()
 
 
+def measured_mfma_peak():
+    """Dense MFMA TFLOP/s this part sustains in the attention kernel's launch
+    shape (4 wavefronts per CU, independent chains), from the microbenchmark
+    library next to the package: {"bf16": ..., "fp8": ...}, or None if it is
+    not built."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_long_scores_amd", "libfp2_microbench.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.fp2_microbench_mfma_tflops
+    fn.restype = ctypes.c_double
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    # best of three runs: the clock settles over the first ones
+    res = {"bf16": round(max(fn(0, 20000, 5) for _ in range(3)), 1),
+           "fp8": round(max(fn(1, 10000, 5) for _ in range(3)), 1)}
+    return res if min(res.values()) > 0 else None
+
+
 def kernel_source_hash():
     """Hash of the HIP sources; HBM traffic read from profiles/ is reported only
     if it was measured on the same sources."""
@@ -422,6 +441,8 @@ def main():
                          sparse_vs_dense_rel_l2=L.sparse_vs_dense())
         log(f"[bench] dense {dense_ms:.3f} ms")
     achieved = F["executed"] / att_ms / 1e9   # TFLOP/s
+    mfma_peak = measured_mfma_peak()
+    log(f"[bench] measured MFMA peak {mfma_peak} TFLOP/s")
     del L, q, k, v
     torch.cuda.empty_cache()
 
@@ -430,6 +451,9 @@ def main():
         wf = synth.WORKLOADS["llama8b_s128k_fp8"]
         levels = [(sp, taus[f"llama8b_s128k_fp8@{sp:.2f}"]["tau"]) for sp in wf["sparsity"]]
         res_fp8 = fp8_legs(fp2, prob, hq, hkv, d, b, S, args.steps, args.warmup, args.dense_steps, stream, levels)
+        if mfma_peak:
+            for lv in res_fp8["levels"].values():
+                lv["frac_of_measured_fp8"] = round(lv["eff_tflops_executed_attn"] / mfma_peak["fp8"], 4)
         torch.cuda.empty_cache()
 
     res_paged = None
@@ -463,7 +487,9 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                     "kernel": "attn_kernel<128,128,bf16> (fp2_sparse_prefill)"},
+                     "kernel": "attn_kernel<128,128,bf16> (fp2_sparse_prefill)",
+                     "peak_measured": mfma_peak,
+                     "frac_of_measured": round(achieved / mfma_peak["bf16"], 4) if mfma_peak else None},
         "cpu_baseline": cpu,
         "breakdown": {
             "select_ms": round(sel_ms, 3),

@@ -1,4 +1,5 @@
 """Build libfp2.so (HIP for gfx950) in-tree: ``python -m block_sparse_long_scores_amd.build``.
+Also builds libfp2_microbench.so, the MFMA-peak microbenchmark bench.py reports.
 
 Every source is compiled with hipcc for gfx950 only, with packed fp32 VALU
 instructions disabled (the kernels never rely on them), and linked into one
@@ -16,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp2.so")
+# the MFMA microbenchmark the benchmark report measures the part's matrix
+# peak with (not part of the library's interface)
+MICRO_SRC = os.path.join(PKG, "microbench", "mfma_peak.hip")
+MICRO_LIB = os.path.join(PKG, "libfp2_microbench.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
@@ -71,6 +76,12 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    tmp = MICRO_LIB + ".tmp"
+    cmd = [hipcc()] + COMMON + ["-shared", MICRO_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("microbenchmark build failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, MICRO_LIB)
     return LIB
 
 
