@@ -126,7 +126,7 @@ def select(S, q_block_ids, tau):
 
 
 def pool_q_heads(q, seqlen_k, block):
-    """Per-query-head block means (selection variant "union"): qbar_heads
+    """Per-query-head block means (selection variants "union" and "max"): qbar_heads
     [Hq, nqb, d], each the mean over the rows of block i present in this call."""
     Sq, Hq, d = q.shape
     geo = geometry(Sq, seqlen_k, block)
@@ -151,6 +151,24 @@ def select_union(qbar_heads, kbar, q_block_ids, tau):
     S = block_scores(qbar_heads, kbar_heads, q_block_ids)
     kept_heads, thr = select(S, q_block_ids, tau)
     kept = kept_heads.reshape(Hkv, G, *kept_heads.shape[1:]).any(axis=1)
+    return kept, S, thr
+
+
+def select_head_max(qbar_heads, kbar, q_block_ids, tau):
+    """Selection variant "max" (another reading of how a GQA group's heads
+    share one mask, [EXP] §2.2 PackGQA with the selection of §2.1): the
+    group's block score is the largest of its query heads' scores,
+    S_ij = max_{hq in group} <qbar_hq,i, kbar_j>, and the max-threshold rule
+    of step 2 runs on that score (plus the sink and diagonal blocks).  The
+    group-mean reading averages the same per-head scores instead, since the
+    score is linear in qbar.  Returns kept [Hkv, nqb, nkb], the group scores
+    S [Hkv, nqb, nkb] and thresholds [Hkv, nqb]."""
+    Hq = qbar_heads.shape[0]
+    Hkv = kbar.shape[0]
+    G = Hq // Hkv
+    S_heads = block_scores(qbar_heads, np.repeat(kbar, G, axis=0), q_block_ids)
+    S = S_heads.reshape(Hkv, G, *S_heads.shape[1:]).max(axis=1)   # NaN (invisible) stays NaN
+    kept, thr = select(S, q_block_ids, tau)
     return kept, S, thr
 
 
@@ -291,7 +309,8 @@ def sparse_prefill(q, k, v, num_kv_heads, block, tau, scale=None,
     """The whole pipeline on one sequence: pool, score, select, attend.
     select_mode "mean": one query mean per GQA group (the default reading);
     "union": per-query-head selection, united over the group (S and thr are
-    then per query head)."""
+    then per query head); "max": the group's score is the largest of its
+    heads' scores (S and thr per KV head, as for "mean")."""
     d = q.shape[2]
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
@@ -300,9 +319,14 @@ def sparse_prefill(q, k, v, num_kv_heads, block, tau, scale=None,
     if select_mode == "union":
         qbar = pool_q_heads(q, k.shape[0], block)
         kept, S, thr = select_union(qbar, kbar, geo.q_block_ids(), tau)
-    else:
+    elif select_mode == "max":
+        qbar = pool_q_heads(q, k.shape[0], block)
+        kept, S, thr = select_head_max(qbar, kbar, geo.q_block_ids(), tau)
+    elif select_mode == "mean":
         S = block_scores(qbar, kbar, geo.q_block_ids())
         kept, thr = select(S, geo.q_block_ids(), tau)
+    else:
+        raise ValueError(f"unknown select_mode {select_mode!r}")
     O, LSE = attend(q, k, v, kept, kbar, vbar, n_k, num_kv_heads, block,
                     scale, mean_correction, q_blocks)
     return dict(geo=geo, qbar=qbar, kbar=kbar, vbar=vbar, n_k=n_k, S=S,

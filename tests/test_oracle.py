@@ -8,6 +8,7 @@ axis, a wrong GQA head mapping) fails at least one of them.
 """
 
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -16,11 +17,18 @@ import torch
 import oracle
 from oracle import attention as A
 
-RNG = np.random.default_rng(12345)
+_STATE = {"rng": np.random.default_rng(12345)}
 
 
-def _rand(*shape, scale=1.0, rng=RNG):
-    return rng.standard_normal(shape) * scale
+@pytest.fixture(autouse=True)
+def _per_test_generator(request):
+    """Each test draws from its own generator, seeded by its name, so the
+    inputs a test sees do not depend on which tests ran before it."""
+    _STATE["rng"] = np.random.default_rng(zlib.crc32(request.node.name.encode()))
+
+
+def _rand(*shape, scale=1.0):
+    return _STATE["rng"].standard_normal(shape) * scale
 
 
 # ------------------------------------------------------------------ e4m3
@@ -248,6 +256,102 @@ def test_select_union_reductions():
     assert np.all(ku >= kh.reshape(Hkv, G, *kh.shape[1:]).any(axis=1))
     assert ku[:, :, 0].all() and ku[:, np.arange(len(ids)), ids].all()
     ki, _, _ = A.select_union(qh, kbar, ids, np.inf)
+    assert A.sparsity(ki, ids) == 0.0
+
+
+def _brute_head_max(q, k, Hkv, b, tau):
+    """Group score = the largest per-head score, with explicit loops: head hq
+    pools its own rows of each query block; the group keeps block j when that
+    maximum is within tau of the row's largest maximum."""
+    Sq, Hq, d = q.shape
+    Sk = k.shape[0]
+    G = Hq // Hkv
+    P = Sk - Sq
+    first, last = P // b, (Sk - 1) // b
+    nkb = -(-Sk // b)
+    kept = np.zeros((Hkv, last - first + 1, nkb), dtype=bool)
+    for h in range(Hkv):
+        for il, i in enumerate(range(first, last + 1)):
+            rows = [r for r in range(Sq) if (P + r) // b == i]
+            s = []
+            for j in range(i + 1):
+                keys = [c for c in range(Sk) if c // b == j]
+                km = [sum(k[c, h, t] for c in keys) / len(keys) for t in range(d)]
+                best = -np.inf
+                for hq in range(h * G, (h + 1) * G):
+                    qm = [sum(q[r, hq, t] for r in rows) / len(rows) for t in range(d)]
+                    best = max(best, sum(qm[t] * km[t] for t in range(d)))
+                s.append(best)
+            m = max(s)
+            for j in range(i + 1):
+                if s[j] >= m - tau or j == 0 or j == i:
+                    kept[h, il, j] = True
+    return kept
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.4, 2.0])
+def test_select_head_max_matches_loops(tau):
+    Sq, Sk, Hq, Hkv, d, b = 21, 37, 6, 2, 3, 4
+    q, k = _rand(Sq, Hq, d), _rand(Sk, Hkv, d)
+    geo = A.geometry(Sq, Sk, b)
+    qh = A.pool_q_heads(q, Sk, b)
+    _, kbar, _, _ = A.pool(q, k, k, Hkv, b)
+    kept, S, thr = A.select_head_max(qh, kbar, geo.q_block_ids(), tau)
+    assert np.array_equal(kept, _brute_head_max(q, k, Hkv, b, tau))
+    assert S.shape == (Hkv, geo.nqb, geo.nkb) and thr.shape == (Hkv, geo.nqb)
+    if tau == 0.4:
+        # the case tells the variants apart: a max that averaged or united instead would fail
+        ku, _, _ = A.select_union(qh, kbar, geo.q_block_ids(), tau)
+        qbar, _, _, _ = A.pool(q, k, k, Hkv, b)
+        km, _ = A.select(A.block_scores(qbar, kbar, geo.q_block_ids()), geo.q_block_ids(), tau)
+        assert not np.array_equal(kept, ku) and not np.array_equal(kept, km)
+
+
+def test_select_head_max_hand_case():
+    """One KV head, two query heads with pooled queries (1, 0) and (0, 1),
+    key-block means (0,0), (1,1), (3,-3), (-5,-5); row i = 3, tau = 1.5.
+    Per-head scores: head 0 [0, 1, 3, -5], head 1 [0, 1, -3, -5].
+    max: [0, 1, 3, -5], threshold 1.5, keeps {2} + sink + diagonal.
+    mean (qbar (0.5, 0.5)): [0, 1, 0, -5], threshold -0.5, keeps {0, 1, 2, 3}.
+    union: head 0 keeps {2}, head 1 (threshold -0.5) keeps {0, 1}: {0, 1, 2, 3}."""
+    ids = np.arange(4)
+    kbar = np.array([[[0.0, 0.0], [1.0, 1.0], [3.0, -3.0], [-5.0, -5.0]]])
+    qh = np.zeros((2, 4, 2))
+    qh[0, :, 0] = 1.0
+    qh[1, :, 1] = 1.0
+    kept, S, thr = A.select_head_max(qh, kbar, ids, 1.5)
+    assert np.array_equal(S[0, 3], [0.0, 1.0, 3.0, -5.0]) and thr[0, 3] == 1.5
+    assert set(np.flatnonzero(kept[0, 3])) == {0, 2, 3}
+    ku, _, _ = A.select_union(qh, kbar, ids, 1.5)
+    km, _ = A.select(A.block_scores(qh.mean(axis=0, keepdims=True), kbar, ids), ids, 1.5)
+    assert set(np.flatnonzero(ku[0, 3])) == {0, 1, 2, 3} == set(np.flatnonzero(km[0, 3]))
+    # row 1 (blocks 0, 1): both kept as sink and diagonal
+    assert set(np.flatnonzero(kept[0, 1])) == {0, 1} and not kept[0, 1, 2:].any()
+
+
+def test_select_head_max_reductions():
+    Sq = Sk = 48
+    Hkv, d, b = 2, 5, 8
+    k = _rand(Sk, Hkv, d)
+    ids = A.geometry(Sq, Sk, b).q_block_ids()
+    # one head per group, or identical heads: the maximum is the group-mean selection
+    q1 = _rand(Sq, Hkv, d)
+    G = 3
+    qg = np.repeat(_rand(Sq, Hkv, 1, d), G, axis=2).reshape(Sq, Hkv * G, d)
+    for q in (q1, qg):
+        qbar, kbar, _, _ = A.pool(q, k, k, Hkv, b)
+        for tau in [0.0, 0.5, 3.0]:
+            kx, Sx, _ = A.select_head_max(A.pool_q_heads(q, Sk, b), kbar, ids, tau)
+            Sm = A.block_scores(qbar, kbar, ids)
+            km, _ = A.select(Sm, ids, tau)
+            assert np.array_equal(kx, km)
+            np.testing.assert_allclose(Sx, Sm, rtol=1e-12, atol=1e-12)
+    # tau = inf keeps all; sink and diagonal always kept
+    q = _rand(Sq, Hkv * G, d)
+    _, kbar, _, _ = A.pool(q, k, k, Hkv, b)
+    kx, _, _ = A.select_head_max(A.pool_q_heads(q, Sk, b), kbar, ids, -1.0)
+    assert kx[:, :, 0].all() and kx[:, np.arange(len(ids)), ids].all()
+    ki, _, _ = A.select_head_max(A.pool_q_heads(q, Sk, b), kbar, ids, np.inf)
     assert A.sparsity(ki, ids) == 0.0
 
 
