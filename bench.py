@@ -353,7 +353,7 @@ def sweep(fp2, workload, levels, steps, seed):
     L = ContigLayer(fp2, q, k, v, fp2.make_params(hq, hkv, d, b, select_mode="union"), S, hkv, d, b)
     (dense_ms,), _, _ = timed(stream, [L.dense], 2, 1)
     rows = []
-    for mode, corr in (("mean", True), ("mean", False), ("union", True)):
+    for mode, corr in (("mean", True), ("mean", False), ("union", True), ("max", True)):
         for target in levels:
             lo, hi = 0.0, 16.0          # sparsity falls as tau grows
             for _ in range(24):

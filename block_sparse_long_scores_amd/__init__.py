@@ -208,8 +208,9 @@ def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"
     """Build an ``Fp2Params``; fp8 scales are device fp32 tensors (o_scale: one
     element, for out_fp8: e4m3 output codes, value = code * o_scale).  The
     params object holds references to them, so they live as long as it does.
-    select_mode: "mean" (group-mean pooled query) or "union" (per query head,
-    united over the GQA group)."""
+    select_mode: "mean" (group-mean pooled query), "union" (per query head,
+    united over the GQA group) or "max" (the largest of the group's per-head
+    block scores, thresholded once)."""
     p = Fp2Params()
     p.num_q_heads = num_q_heads
     p.num_kv_heads = num_kv_heads
@@ -224,7 +225,7 @@ def make_params(num_q_heads, num_kv_heads, head_dim, block_size, tau=float("inf"
     p.k_scale = k_scale.data_ptr() if k_scale is not None else None
     p.v_scale = v_scale.data_ptr() if v_scale is not None else None
     p.o_scale = o_scale.data_ptr() if o_scale is not None else None
-    p.select_mode = {"mean": 0, "union": 1}[select_mode]
+    p.select_mode = {"mean": 0, "union": 1, "max": 2}[select_mode]
     p._scale_tensors = (q_scale, k_scale, v_scale, o_scale)
     return p
 

@@ -79,8 +79,8 @@ fp2_status check_params(const fp2_params* p) {
     return fail(FP2_EINVAL, "fp8 inputs need q_scale, k_scale and v_scale");
   if (p->mean_correction != 0 && p->mean_correction != 1)
     return fail(FP2_EINVAL, "mean_correction=%d must be 0 or 1", p->mean_correction);
-  if (p->select_mode != 0 && p->select_mode != 1)
-    return fail(FP2_EINVAL, "select_mode=%d must be 0 or 1", p->select_mode);
+  if (p->select_mode < 0 || p->select_mode > 2)
+    return fail(FP2_EINVAL, "select_mode=%d must be 0, 1 or 2", p->select_mode);
   // the pooling kernel's 16-byte tasks per row: a query row of all Hq heads,
   // a key row of K and V of all Hkv heads
   const long esz = p->in_dtype == FP2_FP8_E4M3 ? 1 : 2;
@@ -170,7 +170,7 @@ int32_t fp2_max_seqlen_k(const fp2_params* p) {
 size_t fp2_select_workspace_size(const fp2_params* p, int32_t batch, int32_t seqlen_q, int32_t seqlen_k) {
   if (check_params(p) != FP2_OK || check_lengths(batch, seqlen_q, seqlen_k) != FP2_OK) return 0;
   const int nqb = nq_blocks(seqlen_q, seqlen_k, p->block_size);
-  const int qh = p->select_mode == 1 ? p->num_q_heads : p->num_kv_heads;  // pooled query rows per block
+  const int qh = p->select_mode != 0 ? p->num_q_heads : p->num_kv_heads;  // pooled query rows per block
   return align_up((size_t)batch * qh * nqb * p->head_dim * sizeof(float));
 }
 
@@ -307,7 +307,7 @@ PagedLayout paged_layout(const fp2_params* p, int n, int max_nqb, int max_nkb) {
   const size_t H = p->num_kv_heads, D = p->head_dim;
   size_t off = 0;
   L.qbar = off;
-  const size_t QH = p->select_mode == 1 ? p->num_q_heads : p->num_kv_heads;
+  const size_t QH = p->select_mode != 0 ? p->num_q_heads : p->num_kv_heads;
   off += align_up((size_t)n * QH * max_nqb * D * 4);
   L.kbar = off;
   off += align_up((size_t)n * H * max_nkb * D * 4);
@@ -479,7 +479,7 @@ size_t fp2_workspace_size(const fp2_params* p, int32_t batch, int32_t max_seqlen
   // the pooled-query region of the paged layout is the select workspace of
   // the largest query-block count any (sq <= max_sq, sk <= max_sk) reaches
   const size_t paged = paged_layout(p, batch, nq, nk).total;
-  const size_t qh = p->select_mode == 1 ? p->num_q_heads : p->num_kv_heads;
+  const size_t qh = p->select_mode != 0 ? p->num_q_heads : p->num_kv_heads;
   const size_t sel = align_up((size_t)batch * qh * nq * p->head_dim * sizeof(float));
   return paged > sel ? paged : sel;
 }

@@ -53,7 +53,7 @@ struct PoolArgs {
   float* bsum_k;
   float* bsum_v;
   const int* cached_blocks;
-  int select_mode;          // 1: qbar per query head [B, Hq, nqb_stride, D]
+  int select_mode;          // 1, 2: qbar per query head [B, Hq, nqb_stride, D]
 };
 
 struct SelectArgs {
@@ -65,7 +65,8 @@ struct SelectArgs {
   int Hkv, D, block;
   float tau;
   int rows_per_wg;          // query blocks per workgroup
-  int select_mode;          // 0: group-mean qbar; 1: union over the group's query heads
+  int select_mode;          // 0: group-mean qbar; 1: union over the group's query heads;
+                            // 2: largest of the group's per-head scores
   int Hq;
 };
 

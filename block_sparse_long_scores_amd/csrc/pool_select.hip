@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
       }
     }
     __syncthreads();
-    if (a.select_mode == 1) {  // union selection: one mean per query head
+    if (a.select_mode != 0) {  // union and head-max selection: one mean per query head
       const float inv1 = 1.f / (float)nr;
       for (int o = t; o < a.Hq * D; o += kPoolThreads) {
         const int hq = o / D, dd = o - hq * D;
@@ -221,7 +221,8 @@ constexpr int kSelThreads = 256;
 // max-threshold rule per row, then the kept list in ascending order (with
 // the sink and diagonal blocks).  Group-mean mode scores the group's pooled
 // query once; union mode scores each query head of the group and keeps a
-// block when any head keeps it.
+// block when any head keeps it; head-max mode scores each query head and
+// thresholds the largest of the group's scores.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   extern __shared__ float smem[];
   const int s = blockIdx.z;
@@ -244,14 +245,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const float* kbh = a.kbar + ((long)s * a.Hkv + h) * a.seq.nkb_stride * D;
   // group mean: one pass over the group's pooled query; union: one pass per
-  // query head of the group, each OR-ing its kept blocks into kb
+  // query head of the group, each OR-ing its kept blocks into kb; head max:
+  // one pass per query head, each raising the row's scores to its own
   const bool uni = a.select_mode == 1;
-  const int npass = uni ? a.Hq / a.Hkv : 1;
+  const bool hmax = a.select_mode == 2;
+  const int npass = a.select_mode != 0 ? a.Hq / a.Hkv : 1;
   if (uni)
     for (int o = t; o < nrows * nw; o += kSelThreads) kb[o] = 0u;
 
   for (int pass = 0; pass < npass; ++pass) {
-    const float* qsrc = uni ? a.qbar + (((long)s * a.Hq + h * npass + pass) * a.seq.nqb_stride + il0) * D
+    const float* qsrc = a.select_mode != 0 ? a.qbar + (((long)s * a.Hq + h * npass + pass) * a.seq.nqb_stride + il0) * D
                             : a.qbar + (((long)s * a.Hkv + h) * a.seq.nqb_stride + il0) * D;
     __syncthreads();
     for (int o = t; o < nrows * D; o += kSelThreads) qb[o] = qsrc[o];
@@ -276,11 +279,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
           }
         }
       }
+      // each thread owns the same columns j in every pass
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (r < nrows) sc[r * ncols + j] = acc[r];
+        if (r < nrows) sc[r * ncols + j] = (hmax && pass > 0) ? fmaxf(sc[r * ncols + j], acc[r]) : acc[r];
     }
     __syncthreads();
+    if (hmax && pass + 1 < npass) continue;  // threshold once every head has scored
 
     // per row: max over j <= i, threshold; group mean: ascending compaction
     // right away; union: this head's kept blocks into the row's keep bits

@@ -123,9 +123,14 @@ typedef struct {
    * share one mask): 0 = the group-mean qbar of step 1 above;
    * 1 = per query head: qbar_{hq,i} = mean of head hq's rows of block i,
    * each head applies step 2 to <qbar_{hq,i}, kbar_j>, and the group keeps
-   * the union of its heads' blocks (plus sink and diagonal).  The masks
-   * stay per KV head, since the group shares one K/V tile.  Mode 1 needs
-   * Hq/Hkv times the pooled-query workspace of mode 0.                     */
+   * the union of its heads' blocks (plus sink and diagonal);
+   * 2 = per query head scores <qbar_{hq,i}, kbar_j> as in mode 1, the
+   * group's score is their maximum over the group's heads, and step 2 runs
+   * once on that score (mode 0 is the same with the mean over the heads in
+   * place of the maximum, since the score is linear in qbar).  The masks
+   * stay per KV head, since the group shares one K/V tile.  Modes 1 and 2
+   * need Hq/Hkv times the pooled-query workspace of mode 0.  Other values
+   * are FP2_EINVAL.                                                        */
   int32_t select_mode;
 } fp2_params;
 

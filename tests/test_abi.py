@@ -58,13 +58,14 @@ def test_workspace_sizes():
     assert (mq, mk) == (129, 1024)
     assert fp2.fp2_paged_workspace_size(p, 6, 32768, 131072) > 0
     # per-query-head selection pools every query head: G = 4 times the pooled queries
-    u = params()
-    u.select_mode = 1
-    assert fp2.fp2_select_workspace_size(u, 1, 1024, 1024) == 4 * 2 * 8 * 128 * 4
-    assert fp2.fp2_paged_workspace_size(u, 6, 32768, 131072) > fp2.fp2_paged_workspace_size(p, 6, 32768, 131072)
+    for mode in (1, 2):
+        u = params()
+        u.select_mode = mode
+        assert fp2.fp2_select_workspace_size(u, 1, 1024, 1024) == 4 * 2 * 8 * 128 * 4
+        assert fp2.fp2_paged_workspace_size(u, 6, 32768, 131072) > fp2.fp2_paged_workspace_size(p, 6, 32768, 131072)
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 def test_one_workspace_size_covers_both_paths(mode):
     """fp2_workspace_size(p, batch, max_sq, max_sk) is at least the select
     workspace of every smaller call and the paged workspace of every smaller
@@ -108,10 +109,11 @@ def test_validation_errors():
     assert select(params(num_q_heads=64, num_kv_heads=64)) == fp2.FP2_EUNSUPPORTED
     assert fp2.fp2_max_seqlen_k(params(num_q_heads=128, num_kv_heads=8)) == 0
     assert fp2.fp2_max_seqlen_k(params(num_q_heads=64, num_kv_heads=8)) > 0
-    p = params()
-    p.select_mode = 2
-    assert select(p) == fp2.FP2_EINVAL
-    assert "select_mode" in fp2.last_error()
+    for mode in (3, -1):
+        p = params()
+        p.select_mode = mode
+        assert select(p) == fp2.FP2_EINVAL
+        assert "select_mode" in fp2.last_error()
     p = params()
     p.out_dtype = 7
     assert fp2.fp2_dense_prefill(p, 1, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == fp2.FP2_EUNSUPPORTED

@@ -113,7 +113,7 @@ def _chunk_vs_oracle(seq, lo, hi, hkv, b, tau, mode, corr, o, lse, idx, cnt, lab
     return ref
 
 
-@pytest.mark.parametrize("mode", ["mean", "union"])
+@pytest.mark.parametrize("mode", ["mean", "union", "max"])
 def test_paged_block_sum_cache_chunked_prefill(gpu, mode):
     """Chunked prefill with the key-block sum cache (fp2_sparse_prefill_paged_
     pooled): each chunk's call reads the sums of the full blocks its earlier

@@ -26,8 +26,13 @@ def _config(seed):
     Sk = int(r.integers(b + 1, 2600))
     Sq = int(r.integers(1, Sk + 1)) if r.random() < 0.5 else Sk
     return dict(d=d, b=b, hkv=hkv, hq=G * hkv, Sk=Sk, Sq=Sq, tau=float(r.uniform(0.0, 2.5)),
-                fp8=bool(r.random() < 0.35), union=bool(r.random() < 0.3), corr=bool(r.random() < 0.8),
+                fp8=bool(r.random() < 0.35), mode=_mode(r.random()), corr=bool(r.random() < 0.8),
                 kind=str(r.choice(["planted", "iid"])))
+
+
+def _mode(u):
+    """Selection rule from one uniform draw: 15% union, 15% head max, else group mean."""
+    return "union" if u < 0.15 else "max" if u < 0.3 else "mean"
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -35,7 +40,7 @@ def test_random_config(gpu, seed):
     c = _config(seed)
     print(f"[case] random seed={seed} {c}", flush=True)
     pr = synth.make_problem(c["kind"], 40 + seed, c["Sk"], c["hq"], c["hkv"], c["d"], c["b"], seqlen_q=c["Sq"])
-    mode = "union" if c["union"] else "mean"
+    mode = c["mode"]
     if c["fp8"]:
         qc, qs = synth.quantize_e4m3(pr.q, 1)
         kc, ks = synth.quantize_e4m3(pr.k, 1)
@@ -56,7 +61,7 @@ def test_random_config(gpu, seed):
                            select_mode=mode)
     geo = ref["geo"]
     kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
-    band = A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if c["union"] else A.score_band_mask(ref["S"], ref["thr"])
+    band = A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if mode == "union" else A.score_band_mask(ref["S"], ref["thr"])
     assert not ((kept_gpu != ref["kept"]) & ~band).any()
     O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
                     1 / math.sqrt(c["d"]), c["corr"])
@@ -75,7 +80,7 @@ def _paged_config(seed):
     kv = [int(r.integers(1, 2500)) for _ in range(n)]
     ql = [int(r.integers(1, L + 1)) if r.random() < 0.6 else L for L in kv]
     return dict(d=d, b=b, page=page, hkv=hkv, hq=G * hkv, kv=kv, q=ql, tau=float(r.uniform(0.2, 2.0)),
-                fp8=bool(r.random() < 0.35), union=bool(r.random() < 0.3))
+                fp8=bool(r.random() < 0.35), mode=_mode(r.random()))
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -84,7 +89,7 @@ def test_random_paged_batch(gpu, seed):
     print(f"[case] random paged seed={seed} {c}", flush=True)
     pb = synth.make_paged(60 + seed, c["kv"], c["q"], c["hq"], c["hkv"], c["d"], c["b"], page_size=c["page"],
                           fp8=c["fp8"])
-    mode = "union" if c["union"] else "mean"
+    mode = c["mode"]
     scales = dict(fp8=True, q_scale=pb.q_scale.cuda(), k_scale=pb.k_scale.cuda(), v_scale=pb.v_scale.cuda()) \
         if c["fp8"] else {}
     p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], select_mode=mode, **scales)
@@ -105,7 +110,7 @@ def test_random_paged_batch(gpu, seed):
         ref = A.sparse_prefill(qn, kn, vn, c["hkv"], c["b"], c["tau"], q_blocks=[], select_mode=mode)
         geo = ref["geo"]
         kept_gpu = kept_from_lists(idx[s_, :, :geo.nqb], cnt[s_, :, :geo.nqb], geo.nkb)
-        band = (A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if c["union"]
+        band = (A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if mode == "union"
                 else A.score_band_mask(ref["S"], ref["thr"]))
         assert not ((kept_gpu != ref["kept"]) & ~band).any(), s_
         O, Lr = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
