@@ -1,5 +1,6 @@
 """GPU parity at the full sizes of the benchmark workloads (32K and 128K
-layers in bf16, the 128K layer in FP8, the paged six-sequence batch), in the
+layers in bf16, the 128K layer in FP8 at the three sparsity levels the
+benchmark times, the paged six-sequence batch), in the
 launch configuration bench.py times: the whole layer runs on the GPU through
 the C ABI; the float64 oracle then checks every KV group on its own (pool,
 score and select over the whole sequence -> the group's full block mask;
@@ -54,7 +55,9 @@ def _check_group(h, G, q, k, v, tau, b, idx, cnt, out, lse, fp8, seed, label, al
 
 @pytest.mark.parametrize("workload,fp8,sparsity", [("llama8b_s32k_bf16", False, 0.70),
                                                     ("llama8b_s128k_bf16", False, 0.80),
-                                                    ("llama8b_s128k_fp8", True, 0.80)])
+                                                    ("llama8b_s128k_fp8", True, 0.80),
+                                                    ("llama8b_s128k_fp8", True, 0.85),
+                                                    ("llama8b_s128k_fp8", True, 0.90)])
 def test_fullsize_contiguous(gpu, workload, fp8, sparsity):
     w = synth.WORKLOADS[workload]
     S, hq, hkv, d, b = w["seqlen"], w["hq"], w["hkv"], w["d"], w["block"]
