@@ -17,8 +17,9 @@ With --sweep WORKLOAD it instead prints the sparsity/error sweep of that
 workload (bf16): for each target block sparsity a tau is bisected on the
 GPU's own block counts, and the selection + attention time and the relative
 L2 distance of the output to the in-house dense kernel's are reported for
-three variants: group-mean selection with and without the mean correction,
-and per-query-head (union) selection with it.
+four variants: group-mean selection with and without the mean correction,
+and the two per-query-head selections (union of the heads' blocks; largest
+of the heads' scores) with it.
 """
 
 import argparse
@@ -102,14 +103,19 @@ def measured_mfma_peak():
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources; HBM traffic read from profiles/ is reported only
-    if it was measured on the same sources."""
+    """Hash of the HIP sources with comments and whitespace removed; HBM
+    traffic read from profiles/ is reported only if it was measured on the
+    same code (an edit of a comment leaves the hash as it is)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_long_scores_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            text = open(os.path.join(csrc, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -287,8 +287,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     __syncthreads();
     if (hmax && pass + 1 < npass) continue;  // threshold once every head has scored
 
-    // per row: max over j <= i, threshold; group mean: ascending compaction
-    // right away; union: this head's kept blocks into the row's keep bits
+    // per row: max over j <= i, threshold; group mean and head max:
+    // ascending compaction right away; union: this head's kept blocks into
+    // the row's keep bits
     for (int r = wave; r < nrows; r += kSelThreads / 64) {
       const int il = il0 + r;
       const int i = g.first_qb + il;
