@@ -50,6 +50,8 @@
 #include <atomic>
 #include <map>
 #include <mutex>
+#include <thread>
+#include <tuple>
 #include <type_traits>
 #include <utility>
 
@@ -1252,7 +1254,9 @@ static int compute_units() {
 // scheduler above): a captured launch takes the next capture set in turn;
 // otherwise the stream keeps the set it got at its first launch on this
 // device, sets being handed out in first-use order (past kStreamSlots
-// streams the oldest assignment is taken over).
+// streams the oldest assignment is taken over).  hipStreamPerThread is one
+// handle for a different stream in every host thread, so there the calling
+// thread is part of the key.
 static int sched_slot_for(hipStream_t st) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   const hipError_t ce = hipStreamIsCapturing(st, &cs);
@@ -1263,13 +1267,14 @@ static int sched_slot_for(hipStream_t st) {
   if (ce != hipSuccess) (void)hipGetLastError();  // a refused capture query leaves no error behind
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  using Key = std::tuple<int, hipStream_t, std::thread::id>;
   static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, int> slot_of;
-  static std::pair<int, hipStream_t> owner[64][kStreamSlots];
+  static std::map<Key, int> slot_of;
+  static Key owner[64][kStreamSlots];
   static int next[64];
   const int dv = dev & 63;
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(dev, st);
+  const Key key(dev, st, st == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id());
   const auto it = slot_of.find(key);
   if (it != slot_of.end()) return it->second;
   const int slot = next[dv]++ % kStreamSlots;

@@ -42,7 +42,8 @@
  *    fp2_sparse_prefill and fp2_dense_prefill use one of the library's sets:
  *    each of the first 192 streams a process launches them on gets a set of
  *    its own (reused by that stream's later launches, which run in order;
- *    beyond 192 streams the oldest stream's set is handed on), and a launch
+ *    beyond 192 streams the oldest stream's set is handed on; each host
+ *    thread's hipStreamPerThread counts as a stream of its own), and a launch
  *    captured into a HIP graph gets the next of 64 further sets, which no
  *    eager launch uses.  So launches on different streams may run at once,
  *    and graph replays may run next to eager launches on any stream; one
