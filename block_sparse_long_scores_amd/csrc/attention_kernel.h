@@ -1289,15 +1289,21 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
   if (attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride) > 160 * 1024) return hipErrorInvalidValue;
   if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
-  // once per kernel: the static segment fits the allowance (1) or not (-1),
-  // and the dynamic-LDS limit is raised to everything the allowance leaves
-  // (launches then pass their own size, which never lowers the limit)
-  static std::atomic<int> static_ok{0};
+  // once per kernel and device (a kernel's attributes belong to the device
+  // it runs on): the static segment fits the allowance (1) or not (-1), and
+  // the dynamic-LDS limit is raised to everything the allowance leaves
+  // (launches then pass their own size, which never lowers the limit).
+  // Devices past the first 64 redo this at every launch, which sets the same
+  // value again.
+  static std::atomic<int> static_ok[64];  // zero-initialised (static storage)
   static std::mutex init_mu;
-  int ok = static_ok.load(std::memory_order_acquire);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* const okp = dev < 64 ? &static_ok[dev] : nullptr;
+  int ok = okp ? okp->load(std::memory_order_acquire) : 0;
   if (ok == 0) {
     std::lock_guard<std::mutex> lock(init_mu);
-    ok = static_ok.load(std::memory_order_relaxed);
+    ok = okp ? okp->load(std::memory_order_relaxed) : 0;
     if (ok == 0) {
       hipFuncAttributes fa;
       if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8>) != hipSuccess) return hipErrorInvalidValue;
@@ -1308,7 +1314,7 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
                                                  160 * 1024 - kStaticLdsBytes);
         if (e != hipSuccess) return e;
       }
-      static_ok.store(ok, std::memory_order_release);
+      if (okp) okp->store(ok, std::memory_order_release);
     }
   }
   if (ok < 0) return hipErrorInvalidValue;
