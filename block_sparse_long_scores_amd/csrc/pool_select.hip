@@ -167,22 +167,44 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
       }
     }
   }
-  for (int cc = from_cache ? c1 : c0; cc < c1; ++cc) {
-    const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc, rowbytes);
-    const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc, rowbytes);
-    uint4 w[kMaxChunksPerThread];
+  // rows in groups of kKeyRows: every load of a group is issued before the
+  // first is added (the adds keep the row order, so the sums are the same)
+  constexpr int kKeyRows = 4;
+  int cc = from_cache ? c1 : c0;
+  for (; cc + kKeyRows <= c1; cc += kKeyRows) {
+    uint4 w[kKeyRows][kMaxChunksPerThread];
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c) {
-      int task = t + c * kPoolThreads;
-      if (task < ntask) {
-        const char* row = task < nch ? krow : vrow;
-        int ch = task < nch ? task : task - nch;
-        w[c] = *(const uint4*)(row + ch * 16);
+    for (int u = 0; u < kKeyRows; ++u) {
+      const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc + u, rowbytes);
+      const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc + u, rowbytes);
+#pragma unroll
+      for (int c = 0; c < kMaxChunksPerThread; ++c) {
+        const int task = t + c * kPoolThreads;
+        if (task < ntask) {
+          const char* row = task < nch ? krow : vrow;
+          const int ch = task < nch ? task : task - nch;
+          w[u][c] = *(const uint4*)(row + ch * 16);
+        }
       }
     }
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c)
-      if (t + c * kPoolThreads < ntask) acc_chunk<ESZ>(acc[c], w[c]);
+    for (int u = 0; u < kKeyRows; ++u)
+#pragma unroll
+      for (int c = 0; c < kMaxChunksPerThread; ++c)
+        if (t + c * kPoolThreads < ntask) acc_chunk<ESZ>(acc[c], w[u][c]);
+  }
+  for (; cc < c1; ++cc) {
+    const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc, rowbytes);
+    const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc, rowbytes);
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      const int task = t + c * kPoolThreads;
+      if (task < ntask) {
+        const char* row = task < nch ? krow : vrow;
+        const int ch = task < nch ? task : task - nch;
+        acc_chunk<ESZ>(acc[c], *(const uint4*)(row + ch * 16));
+      }
+    }
   }
   if (csk && !from_cache) {
 #pragma unroll
