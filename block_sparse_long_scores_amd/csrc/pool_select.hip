@@ -282,22 +282,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     for (int o = t; o < nrows * D; o += kSelThreads) qb[o] = qsrc[o];
     __syncthreads();
 
-    // scores S[r][j] = <qbar_r, kbar_j> for all j <= jmax (fp32, fixed fma order)
+    // scores S[r][j] = <qbar_r, kbar_j> for all j <= jmax (fp32, fma over d
+    // in order).  A column's kbar row is loaded eight float4 at a time, all
+    // eight in flight before the first is used; rows past nrows compute on
+    // row 0's query (in bounds, results dropped) so that the fma chain has
+    // no branches.
     for (int j = t; j < ncols; j += kSelThreads) {
       float acc[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
       const float4* krow = (const float4*)(kbh + (long)j * D);
-      for (int d4 = 0; d4 < D / 4; ++d4) {
-        float4 kv = krow[d4];
+      for (int d0 = 0; d0 < D / 4; d0 += 8) {  // D / 4 is 16 or 32
+        float4 kv[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (r < nrows) {
-            float4 qv = *(const float4*)(qb + r * D + 4 * d4);
-            acc[r] = fmaf(qv.x, kv.x, acc[r]);
-            acc[r] = fmaf(qv.y, kv.y, acc[r]);
-            acc[r] = fmaf(qv.z, kv.z, acc[r]);
-            acc[r] = fmaf(qv.w, kv.w, acc[r]);
+        for (int u = 0; u < 8; ++u) kv[u] = krow[d0 + u];
+        __builtin_amdgcn_sched_barrier(0);  // keep the eight loads ahead of their use
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float4 qv = *(const float4*)(qb + (r < nrows ? r : 0) * D + 4 * (d0 + u));
+            acc[r] = fmaf(qv.x, kv[u].x, acc[r]);
+            acc[r] = fmaf(qv.y, kv[u].y, acc[r]);
+            acc[r] = fmaf(qv.z, kv[u].z, acc[r]);
+            acc[r] = fmaf(qv.w, kv[u].w, acc[r]);
           }
         }
       }
