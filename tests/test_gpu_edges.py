@@ -92,16 +92,17 @@ def test_one_row_chunk_after_long_prefix(gpu, Sk):
 
 
 @pytest.mark.slow
-def test_longest_supported_sequence(gpu):
-    """seqlen_k at fp2_max_seqlen_k (2.41M keys at d 128, b 128: the
-    selection's score row and the correction's dropped-block list at their
-    LDS limits), a ragged 334-row chunk at its end; tau 1.0 and -inf."""
+@pytest.mark.parametrize("d,b", [(128, 128), (128, 64), (64, 128)])
+def test_longest_supported_sequence(gpu, d, b):
+    """seqlen_k at fp2_max_seqlen_k (2.38M keys at d 128, b 128; 1.83M at
+    b 64; 3.65M at d 64: the selection's score row and the correction's
+    dropped-block list at their LDS limits, which differ per instance), a
+    ragged 334-row chunk at its end; tau 1.0 and -inf."""
     hq = hkv = 1
-    d = b = 128
     Sk = gpu.fp2_max_seqlen_k(gpu.make_params(hq, hkv, d, b))
     Sq = 334
     pr = synth.make_problem("planted", 7, Sk, hq, hkv, d, b, seqlen_q=Sq)
-    print(f"[case] longest sequence planted seed=7 Sk={Sk} Sq={Sq}", flush=True)
+    print(f"[case] longest sequence planted seed=7 d={d} b={b} Sk={Sk} Sq={Sq}", flush=True)
     q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
     qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
     for tau in (1.0, float("-inf")):
