@@ -92,12 +92,13 @@ def test_one_row_chunk_after_long_prefix(gpu, Sk):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("d,b", [(128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("d,b", [(128, 128), (128, 64), (64, 128), (64, 64)])
 def test_longest_supported_sequence(gpu, d, b):
     """seqlen_k at fp2_max_seqlen_k (2.38M keys at d 128, b 128; 1.83M at
-    b 64; 3.65M at d 64: the selection's score row and the correction's
-    dropped-block list at their LDS limits, which differ per instance), a
-    ragged 334-row chunk at its end; tau 1.0 and -inf."""
+    d 128, b 64; 3.65M at d 64, b 128; 2.18M at d 64, b 64: the selection's
+    score row and the correction's dropped-block list at their LDS limits,
+    which differ per instance), a ragged 334-row chunk at its end; tau 1.0
+    and -inf."""
     hq = hkv = 1
     Sk = gpu.fp2_max_seqlen_k(gpu.make_params(hq, hkv, d, b))
     Sq = 334
