@@ -20,6 +20,8 @@
 #include "fp2_internal.h"
 #include "geometry.h"
 
+#include <algorithm>
+
 namespace fp2 {
 
 constexpr int kPoolThreads = 256;
@@ -48,8 +50,14 @@ __device__ __forceinline__ void acc_chunk(float* acc, const uint4& w) {
   }
 }
 
-template <int ESZ>
+// NC: 16-byte chunk slots per thread (a row of W elements is W / EPC chunks
+// over kPoolThreads threads), chosen at launch from the head counts so that
+// no register is held for slots no thread uses; rows are loaded in groups of
+// kRows (fewer when more slots are live), every load of a group in flight
+// before the first is added, in row order.
+template <int ESZ, int NC>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
+  constexpr int kRows = NC == 1 ? 8 : NC == 2 ? 4 : 2;
   constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
   extern __shared__ float red[];
   const int s = blockIdx.y;
@@ -68,37 +76,38 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     const int W = a.Hq * D;
     const int nch = W / EPC;
     const char* base = (const char*)a.q + (long)(g.qrow0 + r0) * W * ESZ;
-    float acc[kMaxChunksPerThread][EPC];
+    float acc[NC][EPC];
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
     const int nr = r1 - r0;
     int r = 0;
-    for (; r + 4 <= nr; r += 4) {
-      uint4 w[4][kMaxChunksPerThread];
+    for (; r + kRows <= nr; r += kRows) {
+      uint4 w[kRows][NC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kRows; ++u)
 #pragma unroll
-        for (int c = 0; c < kMaxChunksPerThread; ++c) {
+        for (int c = 0; c < NC; ++c) {
           int ch = t + c * kPoolThreads;
           if (ch < nch) w[u][c] = *(const uint4*)(base + (long)(r + u) * W * ESZ + ch * 16);
         }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kRows; ++u)
 #pragma unroll
-        for (int c = 0; c < kMaxChunksPerThread; ++c)
+        for (int c = 0; c < NC; ++c)
           if (t + c * kPoolThreads < nch) acc_chunk<ESZ>(acc[c], w[u][c]);
     }
     for (; r < nr; ++r) {
 #pragma unroll
-      for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      for (int c = 0; c < NC; ++c) {
         int ch = t + c * kPoolThreads;
         if (ch < nch) acc_chunk<ESZ>(acc[c], *(const uint4*)(base + (long)r * W * ESZ + ch * 16));
       }
     }
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+    for (int c = 0; c < NC; ++c) {
       int ch = t + c * kPoolThreads;
       if (ch < nch) {
         int e0 = ch * EPC;
@@ -136,9 +145,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   const int nch = W / EPC;
   const int ntask = a.vbar ? 2 * nch : nch;
   const int rowbytes = W * ESZ;
-  float acc[kMaxChunksPerThread][EPC];
+  float acc[NC][EPC];
 #pragma unroll
-  for (int c = 0; c < kMaxChunksPerThread; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
   // block-sum cache (paged): the entry of a full block sits at the physical
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   }
   if (from_cache) {
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const int task = t + c * kPoolThreads;
       if (task < ntask) {
         const bool isv = task >= nch;
@@ -167,18 +176,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
       }
     }
   }
-  // rows in groups of kKeyRows: every load of a group is issued before the
+  // rows in groups of kRows: every load of a group is issued before the
   // first is added (the adds keep the row order, so the sums are the same)
-  constexpr int kKeyRows = 4;
   int cc = from_cache ? c1 : c0;
-  for (; cc + kKeyRows <= c1; cc += kKeyRows) {
-    uint4 w[kKeyRows][kMaxChunksPerThread];
+  for (; cc + kRows <= c1; cc += kRows) {
+    uint4 w[kRows][NC];
 #pragma unroll
-    for (int u = 0; u < kKeyRows; ++u) {
+    for (int u = 0; u < kRows; ++u) {
       const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc + u, rowbytes);
       const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc + u, rowbytes);
 #pragma unroll
-      for (int c = 0; c < kMaxChunksPerThread; ++c) {
+      for (int c = 0; c < NC; ++c) {
         const int task = t + c * kPoolThreads;
         if (task < ntask) {
           const char* row = task < nch ? krow : vrow;
@@ -187,17 +195,18 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < kKeyRows; ++u)
+    for (int u = 0; u < kRows; ++u)
 #pragma unroll
-      for (int c = 0; c < kMaxChunksPerThread; ++c)
+      for (int c = 0; c < NC; ++c)
         if (t + c * kPoolThreads < ntask) acc_chunk<ESZ>(acc[c], w[u][c]);
   }
   for (; cc < c1; ++cc) {
     const char* krow = kv_row(a.kv, a.kv.k, s, a.seq.seqlen_k, cc, rowbytes);
     const char* vrow = kv_row(a.kv, a.kv.v, s, a.seq.seqlen_k, cc, rowbytes);
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const int task = t + c * kPoolThreads;
       if (task < ntask) {
         const char* row = task < nch ? krow : vrow;
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   }
   if (csk && !from_cache) {
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerThread; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const int task = t + c * kPoolThreads;
       if (task < ntask) {
         const bool isv = task >= nch;
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   }
   const float inv = 1.f / (float)(c1 - c0);
 #pragma unroll
-  for (int c = 0; c < kMaxChunksPerThread; ++c) {
+  for (int c = 0; c < NC; ++c) {
     int task = t + c * kPoolThreads;
     if (task < ntask) {
       bool isv = task >= nch;
@@ -376,10 +385,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
   dim3 grid(a.seq.nqb_stride + a.seq.nkb_stride, a.seq.batch);
   size_t lds = (size_t)a.Hq * a.D * sizeof(float);
+  // chunk slots per thread: the larger of the query row (Hq D elements) and
+  // the key block's K (and V) rows, in 16-byte chunks over kPoolThreads
+  const int epc = a.fp8 ? 16 : 8;
+  const int tasks = std::max(a.Hq * a.D / epc, (a.vbar ? 2 : 1) * a.Hkv * a.D / epc);
+  const int nc = (tasks + kPoolThreads - 1) / kPoolThreads;
+  if (nc < 1 || nc > kMaxChunksPerThread) return hipErrorInvalidValue;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kPoolThreads), lds, st, a); };
   if (a.fp8) {
-    hipLaunchKernelGGL(pool_kernel<1>, grid, dim3(kPoolThreads), lds, st, a);
+    if (nc == 1) go(pool_kernel<1, 1>);
+    else if (nc == 2) go(pool_kernel<1, 2>);
+    else if (nc == 3) go(pool_kernel<1, 3>);
+    else go(pool_kernel<1, 4>);
   } else {
-    hipLaunchKernelGGL(pool_kernel<2>, grid, dim3(kPoolThreads), lds, st, a);
+    if (nc == 1) go(pool_kernel<2, 1>);
+    else if (nc == 2) go(pool_kernel<2, 2>);
+    else if (nc == 3) go(pool_kernel<2, 3>);
+    else go(pool_kernel<2, 4>);
   }
   return hipGetLastError();
 }
