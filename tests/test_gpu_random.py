@@ -1,7 +1,9 @@
 """Seeded random configurations against the float64 oracle: sequence and
 chunk lengths, GQA ratio, head dim, block size, threshold, precision,
 selection rule and correction drawn per case (a fixed list, the same on
-every run), covering combinations the targeted tests do not."""
+every run), covering combinations the targeted tests do not; small cases
+(up to 2.6K keys) checked whole, and large ones (4K-24K keys, more tiles
+than compute units) on sampled query blocks."""
 
 import math
 
@@ -118,3 +120,63 @@ def test_random_paged_batch(gpu, seed):
         check_blocks(f64(out[cu[s_]:cu[s_ + 1]]), O, geo, c["hkv"], fp8=c["fp8"],
                      lse=f64(lse[cu[s_]:cu[s_ + 1]]).T, L=Lr,
                      label=f"random paged {seed} seq {s_} Sk={c['kv'][s_]} Sq={c['q'][s_]}")
+
+
+def _large_config(seed):
+    r = np.random.default_rng(5000 + seed)
+    d = int(r.choice([64, 128]))
+    b = int(r.choice([64, 128]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([1, 2, 4, 8]))
+    Sk = int(r.integers(4096, 24000))
+    Sq = Sk if r.random() < 0.6 else int(r.integers(1, Sk + 1))
+    c = dict(d=d, b=b, hkv=hkv, hq=G * hkv, Sk=Sk, Sq=Sq, tau=float(r.uniform(0.8, 2.2)),
+             fp8=bool(r.random() < 0.3), mode=str(r.choice(["mean", "mean", "mean", "union", "max"])),
+             corr=bool(r.random() < 0.85), kind=str(r.choice(["planted", "planted", "iid"])))
+    if c["kind"] == "iid":
+        c["tau"] *= 0.1     # i.i.d. block scores spread ~10x less than planted ones
+    return c
+
+
+# 502 to 5152 tiles per launch: more than the 256 compute units, so that the
+# persistent workgroups take tiles from the tile-queue counters (the small
+# configurations above stay below that)
+@pytest.mark.parametrize("seed", [0, 2, 10, 12, 16, 21, 31, 39])
+def test_random_large_config(gpu, seed):
+    """Seeded configurations of 4K-24K keys: the whole block mask against the
+    oracle, and the outputs and LSE of the first, the last and six seeded
+    query blocks per KV head, each (query block, KV head) on its own."""
+    c = _large_config(seed)
+    print(f"[case] random large seed={seed} {c}", flush=True)
+    pr = synth.make_problem(c["kind"], 900 + seed, c["Sk"], c["hq"], c["hkv"], c["d"], c["b"], seqlen_q=c["Sq"])
+    mode = c["mode"]
+    if c["fp8"]:
+        qc, qs = synth.quantize_e4m3(pr.q, 1)
+        kc, ks = synth.quantize_e4m3(pr.k, 1)
+        vc, vs = synth.quantize_e4m3(pr.v, 1)
+        q, k, v = (t.cuda() for t in (qc, kc, vc))
+        p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], mean_correction=c["corr"], fp8=True,
+                            q_scale=qs.cuda(), k_scale=ks.cuda(), v_scale=vs.cuda(), select_mode=mode)
+        qn, kn, vn = (oracle.dequantize(x.numpy(), y.numpy(), 1) for x, y in ((qc, qs), (kc, ks), (vc, vs)))
+    else:
+        q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+        p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], mean_correction=c["corr"],
+                            select_mode=mode)
+        qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    torch.cuda.synchronize()
+    ref = A.sparse_prefill(qn, kn, vn, c["hkv"], c["b"], c["tau"], mean_correction=c["corr"], q_blocks=[],
+                           select_mode=mode)
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    band = A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if mode == "union" else A.score_band_mask(ref["S"], ref["thr"])
+    assert not ((kept_gpu != ref["kept"]) & ~band).any()
+    ids = geo.q_block_ids()
+    rng = np.random.default_rng(seed)
+    blocks = sorted({int(ids[0]), int(ids[-1]), *(int(x) for x in rng.choice(ids, size=min(6, len(ids)), replace=False))})
+    O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
+                    1 / math.sqrt(c["d"]), c["corr"], q_blocks=blocks)
+    print(f"[random large] sparsity={A.sparsity(kept_gpu, ids):.3f} blocks={blocks}", flush=True)
+    check_blocks(f64(out), O, geo, c["hkv"], fp8=c["fp8"], blocks=blocks, lse=f64(lse[0]), L=L,
+                 label=f"random large {seed}")
