@@ -180,3 +180,61 @@ def test_random_large_config(gpu, seed):
     print(f"[random large] sparsity={A.sparsity(kept_gpu, ids):.3f} blocks={blocks}", flush=True)
     check_blocks(f64(out), O, geo, c["hkv"], fp8=c["fp8"], blocks=blocks, lse=f64(lse[0]), L=L,
                  label=f"random large {seed}")
+
+
+def _large_paged_config(seed):
+    r = np.random.default_rng(7000 + seed)
+    d = int(r.choice([64, 128]))
+    b = int(r.choice([64, 128]))
+    page = int(r.choice([p for p in (16, 32, 64, 128) if p <= b and b // p <= 64]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([1, 4, 8]))
+    n = int(r.integers(2, 6))
+    kv = [int(r.integers(2000, 20000)) for _ in range(n)]
+    ql = [int(r.integers(1, L + 1)) if r.random() < 0.5 else L for L in kv]
+    return dict(d=d, b=b, page=page, hkv=hkv, hq=G * hkv, kv=kv, q=ql, tau=float(r.uniform(0.9, 2.0)),
+                fp8=bool(r.random() < 0.3), mode=str(r.choice(["mean", "mean", "union", "max"])))
+
+
+@pytest.mark.parametrize("seed", [0, 5, 12, 20])
+def test_random_large_paged_batch(gpu, seed):
+    """Seeded continuous batches of 2-5 sequences of 2K-20K keys (chunked
+    prefills among them) over permuted pages of 16-128 tokens: each
+    sequence's whole mask against the oracle, and the outputs and LSE of its
+    first, last and three seeded query blocks per KV head."""
+    c = _large_paged_config(seed)
+    print(f"[case] random large paged seed={seed} {c}", flush=True)
+    pb = synth.make_paged(300 + seed, c["kv"], c["q"], c["hq"], c["hkv"], c["d"], c["b"], page_size=c["page"],
+                          fp8=c["fp8"])
+    mode = c["mode"]
+    scales = dict(fp8=True, q_scale=pb.q_scale.cuda(), k_scale=pb.k_scale.cuda(), v_scale=pb.v_scale.cuda()) \
+        if c["fp8"] else {}
+    p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], select_mode=mode, **scales)
+    out, (idx, cnt), lse = gpu.sparse_prefill_paged(
+        p, pb.q.cuda(), pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda(), max(c["q"]), max(c["kv"]), pb.k_cache.cuda(),
+        pb.v_cache.cuda(), pb.page_table.cuda(), export_mask=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "a canary (NaN) page was read"
+    cu = pb.cu_seqlens_q.numpy()
+    for s_, seq in enumerate(pb.seqs):
+        if c["fp8"]:
+            qn = oracle.dequantize(seq["qc"].numpy(), pb.q_scale.numpy(), 1)
+            kn = oracle.dequantize(seq["kc"].numpy(), pb.k_scale.numpy(), 1)
+            vn = oracle.dequantize(seq["vc"].numpy(), pb.v_scale.numpy(), 1)
+        else:
+            qn, kn, vn = f64(seq["q"]), f64(seq["k"]), f64(seq["v"])
+        ref = A.sparse_prefill(qn, kn, vn, c["hkv"], c["b"], c["tau"], q_blocks=[], select_mode=mode)
+        geo = ref["geo"]
+        kept_gpu = kept_from_lists(idx[s_, :, :geo.nqb], cnt[s_, :, :geo.nqb], geo.nkb)
+        band = (A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if mode == "union"
+                else A.score_band_mask(ref["S"], ref["thr"]))
+        assert not ((kept_gpu != ref["kept"]) & ~band).any(), s_
+        ids = geo.q_block_ids()
+        rng = np.random.default_rng(10 * seed + s_)
+        blocks = sorted({int(ids[0]), int(ids[-1]),
+                         *(int(x) for x in rng.choice(ids, size=min(3, len(ids)), replace=False))})
+        O, Lr = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
+                         1 / math.sqrt(c["d"]), True, q_blocks=blocks)
+        check_blocks(f64(out[cu[s_]:cu[s_ + 1]]), O, geo, c["hkv"], fp8=c["fp8"], blocks=blocks,
+                     lse=f64(lse[cu[s_]:cu[s_ + 1]]).T, L=Lr,
+                     label=f"random large paged {seed} seq {s_} Sk={c['kv'][s_]} Sq={c['q'][s_]}")
