@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from oracle import attention as A
 from tests.helpers import assert_mask_matches, check_blocks, f64, kept_from_lists
@@ -250,3 +251,84 @@ def test_validate_rejects_bad_page_id_before_any_kernel(gpu, monkeypatch, bad):
     print(f"[validate] status {gpu.status_string(st)}: {msg}", flush=True)
     assert st == gpu.FP2_EINVAL and "page id" in msg
     assert bool((out == 7.0).all()), "a kernel ran after the validation error"
+
+
+def _cache_chunking(seed):
+    r = np.random.default_rng(9000 + seed)
+    d = int(r.choice([64, 128]))
+    b = int(r.choice([64, 128]))
+    page = int(r.choice([p for p in (16, 32, 64, 128) if p <= b and b // p <= 64]))
+    hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 4, 8]))
+    n = int(r.integers(1, 4))
+    lens = [int(r.integers(1500, 9000)) for _ in range(n)]
+    nch = int(r.integers(2, 6))
+    bounds = []
+    for Ls in lens:
+        cut = sorted(set(int(x) for x in r.integers(1, Ls, size=nch - 1)))
+        if r.random() < 0.3:   # block-aligned cuts
+            cut = sorted(set(max(b, (x // b) * b) for x in cut))
+        bounds.append([0] + [x for x in cut if 0 < x < Ls] + [Ls])
+    return dict(d=d, b=b, page=page, hkv=hkv, hq=G * hkv, lens=lens, bounds=bounds, tau=float(r.uniform(0.9, 2.0)),
+                fp8=bool(r.random() < 0.3), mode=str(r.choice(["mean", "union", "max"])), corr=bool(r.random() < 0.8))
+
+
+@pytest.mark.parametrize("seed", [5, 8, 10, 16])
+def test_block_sum_cache_random_chunkings(gpu, seed):
+    """Seeded chunked prefills of 1-3 sequences in 2-5 chunks (cuts at random
+    or on block boundaries), bf16 or fp8, any selection rule: in every chunk
+    the cached call equals the uncached one bit for bit (outputs, LSE and the
+    defined mask entries), and each sequence's first and last query block of
+    the chunk match the oracle."""
+    c = _cache_chunking(seed)
+    print(f"[case] block-sum cache random chunking seed={seed} {c}", flush=True)
+    pb = synth.make_paged(500 + seed, c["lens"], c["lens"], c["hq"], c["hkv"], c["d"], c["b"], page_size=c["page"],
+                          fp8=c["fp8"])
+    scales = dict(fp8=True, q_scale=pb.q_scale.cuda(), k_scale=pb.k_scale.cuda(), v_scale=pb.v_scale.cuda()) \
+        if c["fp8"] else {}
+    p = gpu.make_params(c["hq"], c["hkv"], c["d"], c["b"], tau=c["tau"], mean_correction=c["corr"],
+                        select_mode=c["mode"], **scales)
+    kc, vc, tab = pb.k_cache.cuda(), pb.v_cache.cuda(), pb.page_table.cuda()
+    bsk, bsv = gpu.block_sum_cache(p, kc)
+    n = len(c["lens"])
+    cached = torch.zeros(n, dtype=torch.int32, device="cuda")
+    for ck in range(max(len(bd) - 1 for bd in c["bounds"])):
+        act = [s for s in range(n) if ck + 1 < len(c["bounds"][s])]
+        lo = {s: c["bounds"][s][ck] for s in act}
+        hi = {s: c["bounds"][s][ck + 1] for s in act}
+        q = torch.cat([(pb.seqs[s]["qc"] if c["fp8"] else pb.seqs[s]["q"])[lo[s]:hi[s]] for s in act], 0).cuda()
+        cu = [0]
+        for s in act:
+            cu.append(cu[-1] + hi[s] - lo[s])
+        args = (p, q, torch.tensor(cu, dtype=torch.int32, device="cuda"),
+                torch.tensor([hi[s] for s in act], dtype=torch.int32, device="cuda"),
+                max(hi[s] - lo[s] for s in act), max(hi[s] for s in act), kc, vc, tab[act].contiguous())
+        o1, m1, l1 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True)
+        o2, m2, l2 = gpu.sparse_prefill_paged(*args, export_mask=True, return_lse=True,
+                                              pool_cache=(bsk, bsv, cached[act].contiguous()))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"chunk {ck}"
+        _same_masks(m1, m2, [lo[s] for s in act], [hi[s] for s in act], c["b"])
+        for ai, s in enumerate(act):
+            seq = pb.seqs[s]
+            if c["fp8"]:
+                qn = oracle.dequantize(seq["qc"][lo[s]:hi[s]].numpy(), pb.q_scale.numpy(), 1)
+                kn = oracle.dequantize(seq["kc"][:hi[s]].numpy(), pb.k_scale.numpy(), 1)
+                vn = oracle.dequantize(seq["vc"][:hi[s]].numpy(), pb.v_scale.numpy(), 1)
+            else:
+                qn, kn, vn = f64(seq["q"][lo[s]:hi[s]]), f64(seq["k"][:hi[s]]), f64(seq["v"][:hi[s]])
+            ref = A.sparse_prefill(qn, kn, vn, c["hkv"], c["b"], c["tau"], mean_correction=c["corr"], q_blocks=[],
+                                   select_mode=c["mode"])
+            geo = ref["geo"]
+            kept = kept_from_lists(m2[0][ai, :, :geo.nqb], m2[1][ai, :, :geo.nqb], geo.nkb)
+            band = (A.union_band_mask(ref["S"], ref["thr"], c["hkv"]) if c["mode"] == "union"
+                    else A.score_band_mask(ref["S"], ref["thr"]))
+            assert not ((kept != ref["kept"]) & ~band).any(), f"chunk {ck} seq {s}"
+            ids = geo.q_block_ids()
+            blocks = sorted({int(ids[0]), int(ids[-1])})
+            O, L = A.attend(qn, kn, vn, kept, ref["kbar"], ref["vbar"], ref["n_k"], c["hkv"], c["b"],
+                            1 / math.sqrt(c["d"]), c["corr"], q_blocks=blocks)
+            check_blocks(f64(o2[cu[ai]:cu[ai + 1]]), O, geo, c["hkv"], fp8=c["fp8"], blocks=blocks,
+                         lse=f64(l2[cu[ai]:cu[ai + 1]]).T, L=L, label=f"cache chunk {ck} seq {s}")
+        for s in act:
+            cached[s] = hi[s] // c["b"]
