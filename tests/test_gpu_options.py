@@ -103,3 +103,31 @@ def test_null_pooled_buffers(gpu):
             c = int(cnt[0, h, il])
             assert torch.equal(idx2[0, h, il, :c], idx[0, h, il, :c])
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("d,b", [(128, 128), (128, 64), (64, 128), (64, 64)])
+def test_bf16_output_is_the_rounded_fp32_output(gpu, d, b, fp8):
+    """The epilogue's output modes share one normalised value: the bf16
+    output equals round-to-nearest-even of the fp32 output of the same call,
+    bit for bit, in every kernel instance (and in both input precisions)."""
+    hq, hkv, S, Sq = 8, 2, 2500, 1900
+    print(f"[case] bf16 vs fp32 output d={d} b={b} fp8={fp8}", flush=True)
+    pr = synth.make_problem("planted", 17, S, hq, hkv, d, b, seqlen_q=Sq)
+    if fp8:
+        qc, qs = synth.quantize_e4m3(pr.q, 1)
+        kc, ks = synth.quantize_e4m3(pr.k, 1)
+        vc, vs = synth.quantize_e4m3(pr.v, 1)
+        q, k, v = (t.cuda() for t in (qc, kc, vc))
+        sc = dict(fp8=True, q_scale=qs.cuda(), k_scale=ks.cuda(), v_scale=vs.cuda())
+    else:
+        q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+        sc = {}
+    p16 = gpu.make_params(hq, hkv, d, b, tau=0.8, **sc)
+    p32 = gpu.make_params(hq, hkv, d, b, tau=0.8, out_fp32=True, **sc)
+    idx, cnt, pk, pv = gpu.select_blocks(p16, q, k, v)
+    o16 = gpu.sparse_prefill(p16, q, k, v, idx, cnt, pk, pv)
+    o32 = gpu.sparse_prefill(p32, q, k, v, idx, cnt, pk, pv)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16 and o32.dtype == torch.float32
+    assert torch.equal(o16, o32.to(torch.bfloat16))
