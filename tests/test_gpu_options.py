@@ -131,3 +131,40 @@ def test_bf16_output_is_the_rounded_fp32_output(gpu, d, b, fp8):
     torch.cuda.synchronize()
     assert o16.dtype == torch.bfloat16 and o32.dtype == torch.float32
     assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_log_lines_and_unchanged_results(gpu, monkeypatch, capfd):
+    """FP2_LOG=1: each entry point prints one line of its launch shape to
+    stderr (select, sparse and dense attention, the paged call), and the
+    results are the same bits as without it."""
+    hq, hkv, d, b = 8, 2, 128, 128
+    print("[case] FP2_LOG lines", flush=True)
+    pr = synth.make_problem("planted", 18, 3000, hq, hkv, d, b)
+    q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+    p = gpu.make_params(hq, hkv, d, b, tau=0.8)
+    pb = synth.make_paged(19, [1500, 2100], [700, 2100], hq, hkv, d, b, page_size=64)
+    pargs = (p, pb.q.cuda(), pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda(), 2100, 2100, pb.k_cache.cuda(),
+             pb.v_cache.cuda(), pb.page_table.cuda())
+
+    def run():
+        sel = gpu.select_blocks(p, q, k, v)
+        o1 = gpu.sparse_prefill(p, q, k, v, *sel)
+        o2 = gpu.dense_prefill(p, q, k, v)
+        o3 = gpu.sparse_prefill_paged(*pargs)
+        torch.cuda.synchronize()
+        return o1, o2, o3
+
+    monkeypatch.delenv("FP2_LOG", raising=False)
+    ref = run()
+    capfd.readouterr()
+    monkeypatch.setenv("FP2_LOG", "1")
+    got = run()
+    err = capfd.readouterr().err
+    monkeypatch.delenv("FP2_LOG")
+    for a_, b_ in zip(ref, got):
+        assert torch.equal(a_, b_)
+    lines = [ln for ln in err.splitlines() if ln.startswith("[fp2] ")]
+    assert any(ln.startswith("[fp2] select B=1 Sq=3000 Sk=3000 Hq=8 Hkv=2 d=128 b=128") for ln in lines), err
+    assert any(ln.startswith("[fp2] sparse attention B=1 Sq=3000") for ln in lines), err
+    assert any(ln.startswith("[fp2] dense attention B=1 Sq=3000") for ln in lines), err
+    assert any(ln.startswith("[fp2] paged n=2 max_sq=2100 max_sk=2100 page=64") for ln in lines), err
