@@ -57,6 +57,8 @@
  *    call returns a negative fp2_status, enqueues nothing, and
  *    fp2_last_error() (thread-local) describes the problem.  A failed launch
  *    returns FP2_EDEVICE.  No C++ exception crosses this interface.
+ *  - With FP2_LOG=1 in the environment every call prints one line of its
+ *    launch shape to stderr; results are unchanged.
  *  - Numerical range: each query row's softmax runs against a fixed
  *    reference (the largest logit over the first 32 keys of the row's first
  *    kept block, plus a margin) instead of a running maximum.  A row whose
