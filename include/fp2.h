@@ -38,7 +38,10 @@
  *    Only kernels are enqueued (no memset, copy or host synchronisation), so
  *    a call can be captured into a HIP graph.  The attention kernel pulls
  *    its tiles from 8 device-side counters that no concurrent launch may
- *    share.  The paged entry points keep them in the caller's workspace.
+ *    share.  The paged entry points keep them in the caller's workspace
+ *    (with the call's pooled blocks, mask and task list), so a workspace,
+ *    like any output buffer, must not be shared by calls that overlap in
+ *    time; calls on one stream run in order and may reuse it.
  *    fp2_sparse_prefill and fp2_dense_prefill use one of the library's sets:
  *    each of the first 192 streams a process launches them on gets a set of
  *    its own (reused by that stream's later launches, which run in order;
@@ -254,7 +257,9 @@ fp2_status fp2_dense_prefill(const fp2_params* p, int32_t batch,
  *                  [num_seqs, Hkv, max_nqb] with the sizes given by
  *                  fp2_paged_mask_dims; row il of sequence s is its il-th
  *                  query block, as in fp2_select_blocks.
- *   workspace    : at least fp2_paged_workspace_size bytes.                 */
+ *   workspace    : at least fp2_paged_workspace_size bytes; holds the
+ *                  call's pooled blocks, mask, task list and tile-queue
+ *                  counters until the call has run (see the conventions).    */
 void fp2_paged_mask_dims(const fp2_params* p, int32_t max_seqlen_q,
                          int32_t max_seqlen_k, int32_t* max_nqb, int32_t* max_nkb);
 size_t fp2_paged_workspace_size(const fp2_params* p, int32_t num_seqs,
