@@ -266,6 +266,9 @@ def fp8_legs(fp2, prob, hq, hkv, d, b, S, steps, warmup, dense_steps, stream, ta
                                 eff_tflops_executed_attn=round(ach, 1),
                                 frac_fp8_peak=round(ach / PEAK_FP8_TFLOPS, 4),
                                 eff_tflops_dense_equiv=round(F["dense_eq"] / step / 1e9, 1),
+                                # dense-equivalent rate over the peak: above 1 when skipping blocks beats
+                                # computing them, so it is a speed ratio, not a utilisation
+                                dense_equiv_over_fp8_peak=round(F["dense_eq"] / step / 1e9 / PEAK_FP8_TFLOPS, 3),
                                 speedup_vs_fp8_dense=round(dense_ms / step, 2),
                                 sparse_vs_dense_rel_l2=L.sparse_vs_dense())
         log(f"[bench] fp8 @{sp:.2f}: step {step:.3f} ms (select {sel:.3f}, attention {att:.3f}), "
@@ -337,12 +340,16 @@ def paged_leg(fp2, w, tau, steps, warmup, stream, seed):
         vis += vis_s
         executed += 4.0 * d * (G * b) * b * kept_s + 4.0 * d * (G * b) * (vis_s - kept_s)
     ach = executed / ms / 1e9
+    # dense-equivalent: every causal (query, key) pair of the new rows, a chunk of Lq rows after a
+    # prefix of L - Lq keys giving Lq (L - Lq) + Lq (Lq + 1) / 2 pairs
+    dense_eq = 4.0 * d * hq * sum(Lq * (L - Lq) + Lq * (Lq + 1) / 2 for L, Lq in zip(kv_lens, q_lens))
     log(f"[bench] paged batch6: {ms:.3f} ms, sparsity {1 - kept / vis:.4f}, {ach:.0f} TFLOP/s executed; "
         f"with the prefixes' block sums cached {ms_pooled:.3f} ms")
     return dict(ms=round(ms, 3), wall_ms=round(wall, 3), ms_block_sum_cache=round(ms_pooled, 3), tau=round(tau, 5),
                 block_sparsity=round(1 - kept / vis, 4),
                 new_tokens=int(sum(q_lens)), cached_tokens=int(sum(kv_lens)),
                 eff_tflops_executed=round(ach, 1), frac_bf16_peak=round(ach / PEAK_BF16_TFLOPS, 4),
+                dense_equiv_tflop=round(dense_eq / 1e12, 3), eff_tflops_dense_equiv=round(dense_eq / ms / 1e9, 1),
                 note="select + attention in one call (pool, score, select, attend over 64-token permuted pages)")
 
 
@@ -507,6 +514,7 @@ def main():
             "executed_tflop": round(F["executed"] / 1e12, 3),
             "dense_equiv_tflop": round(F["dense_eq"] / 1e12, 3),
             "eff_tflops_dense_equiv": round(F["dense_eq"] / step_ms / 1e9, 1),
+            "dense_equiv_over_bf16_peak": round(F["dense_eq"] / step_ms / 1e9 / PEAK_BF16_TFLOPS, 3),
             "eff_tflops_executed_attn": round(achieved, 1),
             "dense": res_dense,
             "speedup_vs_dense": round(res_dense["ms"] / step_ms, 2) if res_dense else None,
