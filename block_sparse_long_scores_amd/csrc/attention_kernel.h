@@ -199,10 +199,12 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   const int l32 = lane & 31;
 
   // ---- tile (q, pos): position pos of queue q (see attn_kernel).
-  //  Without a plan, tile t = 8*pos + q: query blocks go from the last
-  //  (longest) down; the G2 = Hkv*batch*parts tiles of one query block are
-  //  rotated by the query-block rank, so that queue t % 8 serves every head
-  //  in turn (kept-block counts differ between heads) while the parts of one
+  //  Without a plan, tile t = 8*pos + q: the KV heads go in groups of
+  //  head_group (all heads at once in sparse launches), and within a group
+  //  query blocks go from the last (longest) down; the G2 =
+  //  head_group*batch*parts tiles of one query block are rotated by the
+  //  query-block rank, so that queue t % 8 serves every head of the group in
+  //  turn (kept-block counts differ between heads) while the parts of one
   //  tile share a queue.
   //  With a plan: task k = 8*(pos / parts) + q of the work-ordered list,
   //  part pos % parts.
@@ -216,12 +218,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     h = r / a.seq.nqb_stride;
     il = r - h * a.seq.nqb_stride;
   } else {
-    const int tile = 8 * pos + q;
-    const int G2 = a.Hkv * a.seq.batch * a.parts;
+    const int HG = a.head_group;
+    const int G2 = HG * a.seq.batch * a.parts;
+    const int per_group = G2 * a.nqb_grid;
+    const int tile0 = 8 * pos + q;
+    const int grp = tile0 / per_group;
+    const int tile = tile0 - grp * per_group;
     const int rank = tile / G2;
     int t = (tile - rank * G2 + rank) % G2;
-    h = t % a.Hkv;
-    t /= a.Hkv;
+    h = grp * HG + t % HG;
+    t /= HG;
     s = t % a.seq.batch;
     t /= a.seq.batch;
     part = t;
@@ -1289,6 +1295,8 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
   if (attn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride) > 160 * 1024) return hipErrorInvalidValue;
   if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
+  // the tile order maps every tile to a head below Hkv only for a divisor
+  if (!a0.plan && (a0.head_group < 1 || a0.Hkv % a0.head_group != 0)) return hipErrorInvalidValue;
   // once per kernel and device (a kernel's attributes belong to the device
   // it runs on): the static segment fits the allowance (1) or not (-1), and
   // the dynamic-LDS limit is raised to everything the allowance leaves

@@ -103,6 +103,7 @@ struct AttnArgs {
   int parts;                // workgroups per (seq, head, q-block) tile
   int waves;                // waves per workgroup
   int nqb_grid;             // query-block extent of the tile space
+  int head_group;           // KV heads per group of the tile order (divides Hkv; no plan)
   const int* plan;          // optional work-ordered task list (PlanArgs) or nullptr
   const int* plan_count;
   // tile-queue counters (8 x 32 unsigned, zeroed before the launch) in caller

@@ -125,6 +125,33 @@ def test_tau_inf_sparse_equals_dense(gpu):
     assert torch.equal(out_s, out_d)
 
 
+@pytest.mark.parametrize("batch,S,fp8", [(1, 40960, False), (2, 20480, False), (1, 81920, True)])
+def test_tau_inf_sparse_equals_dense_head_groups(gpu, batch, S, fp8):
+    """Dense launches whose K/V (all heads, over the batch) exceed 128 MiB take
+    the KV heads two at a time; with every block kept, the sparse launch (all
+    heads at once) must still give the same bits, output and LSE."""
+    hq, hkv, d, b = 32, 8, 128, 128
+    prs = [_case("iid", 20 + s, S, hq, hkv, d, b) for s in range(batch)]
+    q, k, v = (torch.stack([getattr(p_, n) for p_ in prs]) for n in ("q", "k", "v"))
+    extra = {}
+    if fp8:
+        q, qs = synth.quantize_e4m3(q[0], 1)
+        k, ks = synth.quantize_e4m3(k[0], 1)
+        v, vs = synth.quantize_e4m3(v[0], 1)
+        q, k, v = q[None], k[None], v[None]
+        extra = dict(fp8=True, q_scale=qs.cuda(), k_scale=ks.cuda(), v_scale=vs.cuda())
+    assert 2 * batch * S * d * (1 if fp8 else 2) * hkv > 128 * 2**20
+    p = gpu.make_params(hq, hkv, d, b, tau=float("inf"), **extra)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out_s, lse_s = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    out_d, lse_d = gpu.dense_prefill(p, q, k, v, return_lse=True)
+    torch.cuda.synchronize()
+    assert (cnt.cpu().numpy() == np.arange(1, cnt.shape[2] + 1)[None, None, :]).all()
+    assert torch.equal(out_s, out_d) and torch.equal(lse_s, lse_d)
+    assert torch.isfinite(out_d.float()).all()
+
+
 def test_run_twice_bit_identical(gpu):
     hq, hkv, d, b, S = 8, 2, 128, 128, 2048
     pr = _case("planted", 5, S, hq, hkv, d, b)
