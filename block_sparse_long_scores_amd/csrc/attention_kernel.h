@@ -725,18 +725,25 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
                     const i32x8 (&k0)[C::KS8], const i32x8 (&k1)[C::KS8], int ntq, f32x16 (&So)[2])
       __attribute__((always_inline)) {
     constexpr int NPVS = C::MT + 1, NSLOT = NPVS + 2 * C::KS8, NPIECE = 10;
+    static_assert(NSLOT == 2 * NPVS - 1, "a stage without QK chains spreads its P V MFMAs over every other slot");
     int bq;
     float bias, mh;
 #pragma unroll
     for (int g = 0; g < NSLOT; ++g) {
       if constexpr (F8) {
-        if (g < C::MT) {
+        // MFMA of slot g; a stage without QK chains (NSLOT = 2 NPVS - 1) puts
+        // its P V MFMAs in every other slot, so that the softmax pieces of
+        // the slots between them issue under an MFMA as well
+        const bool has = qk_on || g % 2 == 0;
+        const int mi = qk_on ? g : g / 2;
+        if (!has) {
+        } else if (mi < C::MT) {
           if (pv_on)
-            O[g][ntp] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv[g], pp, O[g][ntp], 0, 0, 0, 127, 0, psb);
-        } else if (g == C::MT) {
+            O[mi][ntp] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vv[mi], pp, O[mi][ntp], 0, 0, 0, 127, 0, psb);
+        } else if (mi == C::MT) {
           if (pv_on) Lacc[ntp] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pp, Lacc[ntp], 0, 0, 0, 127, 0, psb);
         } else if (qk_on) {
-          const int t = g - NPVS;
+          const int t = mi - NPVS;
           if constexpr (C::KS8 == 2) {
             if (t == 0) qk8_first(So[0], k0[0], qop[ntq][0]);
             if (t == 1) qk8_first(So[1], k1[0], qop[ntq][0]);
