@@ -645,33 +645,35 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     return S;
   };
   // Superchunk softmax of column set nt (Sn[q] is the S^T chunk 2sc + q), in
-  // pieces: sm8_scale(q) applies the causal mask (mode 1) to chunk q and
-  // takes its max, and for q = 1 the superchunk's power-of-two scale (one
-  // scale per 64 keys: the max-tree tail and the scale arithmetic run once
-  // instead of per chunk); sm8_exp(q, j) turns registers 4j..4j+3 of chunk q
-  // into 4 scaled e4m3 bytes of P.
+  // pieces: sm8_scale(q) for q = 0, 1 applies the causal mask (mode 1) to
+  // chunk q and folds its max into mh, and for q = 2 takes the other lane
+  // half's max and sets the superchunk's power-of-two scale (one scale per
+  // 64 keys: the max-tree tail and the scale arithmetic run once instead of
+  // per chunk, in a slot of their own, as they are a chain of dependent
+  // ops); sm8_exp(q, j) turns registers 4j..4j+3 of chunk q into 4 scaled
+  // e4m3 bytes of P.
   auto sm8_scale = [&](f32x16 (&Sn)[2], int q, int nt, int sc, int mode, float& mh, int& bq, float& bias)
       __attribute__((always_inline)) {
-    if (mode == 1) {
+    if (q < 2) {
+      if (mode == 1) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
-        if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int kic = 8 * (r >> 2) + 4 * hh + (r & 3);
+          if ((2 * sc + q) * 32 + kic > rib[nt]) Sn[q][r] = -INFINITY;
+        }
       }
-    }
-    // NaN-propagating maximum (v_maximum3_f32, no canonicalizing copies of
-    // the MFMA results, which fmaxf needs in IEEE mode): 16 values in 8 ops;
-    // chunk 1 then takes chunk 0's and the other lane half's 16 keys of the
-    // same query column, and sets the superchunk's scale
-    const f32x16& v = Sn[q];
-    const float m0 = maximum3(v[0], v[1], v[2]), m1 = maximum3(v[3], v[4], v[5]);
-    const float m2 = maximum3(v[6], v[7], v[8]), m3 = maximum3(v[9], v[10], v[11]);
-    const float m4 = maximum3(v[12], v[13], v[14]);
-    if (q == 0) {
-      mh = maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), v[15]);
+      // NaN-propagating maximum (v_maximum3_f32, no canonicalizing copies
+      // of the MFMA results, which fmaxf needs in IEEE mode): 16 values in 8
+      // ops; chunk 1 folds in chunk 0's
+      const f32x16& v = Sn[q];
+      const float m0 = maximum3(v[0], v[1], v[2]), m1 = maximum3(v[3], v[4], v[5]);
+      const float m2 = maximum3(v[6], v[7], v[8]), m3 = maximum3(v[9], v[10], v[11]);
+      const float m4 = maximum3(v[12], v[13], v[14]);
+      mh = maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), q == 0 ? v[15] : mh);
       return;
     }
-    const float m = max_partner32(maximum3(maximum3(m0, m1, m2), maximum3(m3, m4, v[15]), mh));
+    // the other lane half's 16 keys of the same query column, then the scale
+    const float m = max_partner32(mh);
     const float rel = __builtin_fmaf(m, cs[nt], -mref[nt]);
     rmax[nt] = fmaxf(rmax[nt], rel);
     float fx = floorf(rel);
@@ -718,13 +720,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   // One fp8 stage in issue order, each slot pinned by a scheduling barrier:
   // the P V MFMAs of column set ntp (its O tiles, then the row-sum MFMA),
   // then the two QK chains of column set ntq (first MFMAs, then last ones);
-  // after each slot one piece of the softmax of column set nts (the two
-  // scales first, then the eight 4-score groups).
+  // after each slot one or two pieces of the softmax of column set nts (the
+  // two max trees and the scale first, then the eight 4-score groups).
   auto stage8 = [&](f32x16 (&Sn)[2], int nts, int sc, int mode, i32x8& pk, int& sbyte, bool pv_on,
                     const i32x8 (&vv)[C::MT], const i32x8& pp, int psb, int ntp, bool qk_on,
                     const i32x8 (&k0)[C::KS8], const i32x8 (&k1)[C::KS8], int ntq, f32x16 (&So)[2])
       __attribute__((always_inline)) {
-    constexpr int NPVS = C::MT + 1, NSLOT = NPVS + 2 * C::KS8, NPIECE = 10;
+    constexpr int NPVS = C::MT + 1, NSLOT = NPVS + 2 * C::KS8, NPIECE = 11;
     static_assert(NSLOT == 2 * NPVS - 1, "a stage without QK chains spreads its P V MFMAs over every other slot");
     int bq;
     float bias, mh;
@@ -755,13 +757,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
           }
         }
       }
+      // pieces 0-2 (the two max trees, then the scale) in slots 0-2, the 8
+      // code pieces spread over the remaining slots, the later slots taking
+      // two where there are more pieces than slots
 #pragma unroll
       for (int pc = 0; pc < NPIECE; ++pc) {
-        if ((pc < NSLOT ? pc : NSLOT - 1) == g) {
-          if (pc < 2) {
+        if ((pc < 3 ? pc : NSLOT - 1 - (10 - pc) * (NSLOT - 3) / 8) == g) {
+          if (pc < 3) {
             sm8_scale(Sn, pc, nts, sc, mode, mh, bq, bias);
           } else {
-            sm8_exp(Sn, (pc - 2) >> 2, (pc - 2) & 3, nts, bias, pk);
+            sm8_exp(Sn, (pc - 3) >> 2, (pc - 3) & 3, nts, bias, pk);
           }
         }
       }
