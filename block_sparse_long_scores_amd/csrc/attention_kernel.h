@@ -186,8 +186,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 // One tile: the G*b packed query rows of (sequence, KV head, query block) or
 // the 256-row part `part` of them, over its kept key blocks (or all blocks
-// j <= i when dense), then the mean correction and the epilogue.
-template <int D, int BLK, bool F8>
+// j <= i when dense), then the mean correction and the epilogue.  PG: a
+// paged launch (K/V rows through the page table, tiles in the plan's work
+// order); contiguous launches get an instance without any of the page-table
+// code, which leaves their block loop shorter and their registers freer.
+template <int D, int BLK, bool F8, bool PG>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const int pos, char* smem) {
   using C = Cfg<D, BLK, F8>;
   const int tid = threadIdx.x;
@@ -209,7 +212,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   //  With a plan: task k = 8*(pos / parts) + q of the work-ordered list,
   //  part pos % parts.
   int h, s, part, il;
-  if (a.plan) {
+  if constexpr (PG) {
     part = pos % a.parts;
     const int task = a.plan[8 * (pos / a.parts) + q];
     const int per_seq = a.Hkv * a.seq.nqb_stride;
@@ -313,7 +316,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   const int rowbytes = a.Hkv * C::ROWB;
   const int Skm1 = g.Sk - 1;
   const int plog = a.kv.page_log2;
-  const int* ptab = a.kv.page_table ? a.kv.page_table + (long)s * a.kv.max_pages : nullptr;
+  const int* ptab = PG ? a.kv.page_table + (long)s * a.kv.max_pages : nullptr;
 
   // Paged caches: page ids of key block j, lane i holding the id of its i-th
   // page (a block spans BLK / page_size <= 64 pages; page_size divides BLK).
@@ -1180,7 +1183,7 @@ __global__ void sched_reset_kernel(int slot) {
   if (threadIdx.x < 8) atomicExch(&g_sched[slot][threadIdx.x][0], 0u);
 }
 
-template <int D, int BLK, bool F8>
+template <int D, int BLK, bool F8, bool PG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -1188,9 +1191,9 @@ void attn_kernel(AttnArgs a) {
   const int home = blockIdx.x & 7;
   unsigned int(*ctr)[32] = a.sched ? (unsigned int(*)[32])a.sched : g_sched[a.sched_slot];
   // tiles in queue q: all positions below it are tiles
-  const int ntask = a.plan ? __builtin_amdgcn_readfirstlane(a.plan_count[0]) : a.ntiles;
+  const int ntask = PG ? __builtin_amdgcn_readfirstlane(a.plan_count[0]) : a.ntiles;
   auto queue_len = [&](int q) -> int {
-    if (!a.plan) return (ntask - q + 7) >> 3;
+    if (!PG) return (ntask - q + 7) >> 3;
     return q < ntask ? ((ntask - q + 7) >> 3) * a.parts : 0;
   };
   // next-tile broadcast, double-buffered: the slot written at iteration k is
@@ -1220,7 +1223,7 @@ void attn_kernel(AttnArgs a) {
   }
   for (int k = 0; tile >= 0; ++k) {
     if (threadIdx.x == 0 && qi < 8) pre = atomicAdd(&ctr[(home + qi) & 7][0], 1u);
-    attn_tile<D, BLK, F8>(a, tile & 7, tile >> 3, smem);
+    attn_tile<D, BLK, F8, PG>(a, tile & 7, tile >> 3, smem);
     if (threadIdx.x == 0) next_slot[k & 1] = next_tile();
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(next_slot[k & 1]);
@@ -1302,6 +1305,35 @@ static int sched_slot_for(hipStream_t st) {
   return slot;
 }
 
+// Once per kernel instance and device (a kernel's attributes belong to the
+// device it runs on): whether the static segment fits the allowance (1) or
+// not (-1), after raising the dynamic-LDS limit to everything the allowance
+// leaves (launches then pass their own size, which never lowers the limit);
+// 0 when the attributes cannot be read.  Devices past the first 64 redo this
+// at every launch, which sets the same value again.
+template <int D, int BLK, bool F8, bool PG>
+static int lds_attr_ok() {
+  static std::atomic<int> static_ok[64];  // zero-initialised (static storage)
+  static std::mutex init_mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* const okp = dev < 64 ? &static_ok[dev] : nullptr;
+  int ok = okp ? okp->load(std::memory_order_acquire) : 0;
+  if (ok != 0) return ok;
+  std::lock_guard<std::mutex> lock(init_mu);
+  ok = okp ? okp->load(std::memory_order_relaxed) : 0;
+  if (ok != 0) return ok;
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8, PG>) != hipSuccess) return 0;
+  ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
+  if (ok > 0 && hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8, PG>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024 - kStaticLdsBytes) != hipSuccess)
+    return 0;
+  if (okp) okp->store(ok, std::memory_order_release);
+  return ok;
+}
+
 template <int D, int BLK, bool F8>
 static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   const long ntiles = (long)a0.Hkv * a0.seq.batch * a0.parts * a0.nqb_grid;
@@ -1309,35 +1341,10 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
   if (ntiles > 0x7fffffffL) return hipErrorInvalidValue;
   // the tile order maps every tile to a head below Hkv only for a divisor
   if (!a0.plan && (a0.head_group < 1 || a0.Hkv % a0.head_group != 0)) return hipErrorInvalidValue;
-  // once per kernel and device (a kernel's attributes belong to the device
-  // it runs on): the static segment fits the allowance (1) or not (-1), and
-  // the dynamic-LDS limit is raised to everything the allowance leaves
-  // (launches then pass their own size, which never lowers the limit).
-  // Devices past the first 64 redo this at every launch, which sets the same
-  // value again.
-  static std::atomic<int> static_ok[64];  // zero-initialised (static storage)
-  static std::mutex init_mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  std::atomic<int>* const okp = dev < 64 ? &static_ok[dev] : nullptr;
-  int ok = okp ? okp->load(std::memory_order_acquire) : 0;
-  if (ok == 0) {
-    std::lock_guard<std::mutex> lock(init_mu);
-    ok = okp ? okp->load(std::memory_order_relaxed) : 0;
-    if (ok == 0) {
-      hipFuncAttributes fa;
-      if (hipFuncGetAttributes(&fa, (const void*)attn_kernel<D, BLK, F8>) != hipSuccess) return hipErrorInvalidValue;
-      ok = fa.sharedSizeBytes <= (size_t)kStaticLdsBytes ? 1 : -1;
-      if (ok > 0) {
-        const hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<D, BLK, F8>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 160 * 1024 - kStaticLdsBytes);
-        if (e != hipSuccess) return e;
-      }
-      if (okp) okp->store(ok, std::memory_order_release);
-    }
-  }
-  if (ok < 0) return hipErrorInvalidValue;
+  const bool pg = a0.kv.page_table != nullptr;
+  if (pg != (a0.plan != nullptr)) return hipErrorInvalidValue;  // paged launches come with their plan
+  const int ok = pg ? lds_attr_ok<D, BLK, F8, true>() : lds_attr_ok<D, BLK, F8, false>();
+  if (ok <= 0) return hipErrorInvalidValue;
   const size_t lds_total = attn_dyn_lds_bytes<D, BLK, F8>(a0.seq.nkb_stride);
   if (ntiles == 0) return hipSuccess;
   AttnArgs a = a0;
@@ -1351,7 +1358,10 @@ static hipError_t launch_t(const AttnArgs& a0, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((attn_kernel<D, BLK, F8>), dim3((unsigned)grid), dim3(64 * a.waves), lds_total, st, a);
+  if (pg)
+    hipLaunchKernelGGL((attn_kernel<D, BLK, F8, true>), dim3((unsigned)grid), dim3(64 * a.waves), lds_total, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, BLK, F8, false>), dim3((unsigned)grid), dim3(64 * a.waves), lds_total, st, a);
   return hipGetLastError();
 }
 
