@@ -80,6 +80,13 @@ constexpr float kRefUnder = 60.0f;
 // linear in the fraction of x).  The shift centres its error: the decoded
 // code is within a factor exp(+-0.0728) of 2^x over the normal range.
 constexpr float kCodeShift = 0.34f;
+// The code c is converted two scores at a time as the unorm16 fraction
+// (256 c + 127.5) / 65535: the high byte of round(65535 y) is then c rounded
+// to nearest, and one byte permute gathers four such high bytes into the
+// packed P operand (two packed converts and a permute per four scores, in
+// place of four single-byte converts).
+constexpr float kU16 = 256.0f / 65535.0f;
+constexpr float kU16Half = 127.5f / 65535.0f;
 
 template <int D, int BLK, bool F8>
 struct Cfg {
@@ -298,9 +305,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   f32x16 O[C::MT][NT];
   f32x16 Lacc[F8 ? NT : 1];  // fp8: row sums of P, accumulated by MFMA
   float mref[NT], lsum[NT];
-  // fp8: 8 * logit scale; 56 - kCodeShift - 8 * mref (the code offset of
-  // the pass's reference); the largest superchunk maximum above mref (log2
-  // units) seen in the pass, which sets the exact reference of a rerun.
+  // fp8: 8 * logit scale and 56 - kCodeShift - 8 * mref (the code offset of
+  // the pass's reference), both in unorm16 units (times kU16, the offset
+  // plus kU16Half); the largest superchunk maximum above mref (log2 units)
+  // seen in the pass, which sets the exact reference of a rerun.
   float cs8[F8 ? NT : 1], base8[F8 ? NT : 1], rmax[F8 ? NT : 1];
   // rerun search step per row (log2 units; negative once bracketed)
   float rstep[NT];
@@ -308,7 +316,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   for (int nt = 0; nt < NT; ++nt) rstep[nt] = kFirstStep;
   if constexpr (F8) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) cs8[nt] = 8.f * cs[nt];
+    for (int nt = 0; nt < NT; ++nt) cs8[nt] = (8.f * kU16) * cs[nt];
   }
 
   // LDS: K tiles at [0, 2*TILE), V tiles at [2*TILE, 4*TILE) (double buffer)
@@ -682,11 +690,13 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     float fx = floorf(rel);
     fx = fminf(fmaxf(fx, -110.f), 120.f);
     bq = (int)fx - 7;
-    bias = __builtin_fmaf(-8.f, (float)bq, base8[nt]);  // code offset: 8 (7 - mref - bq) - kCodeShift
+    bias = __builtin_fmaf(-8.f * kU16, (float)bq, base8[nt]);  // code offset 8 (7 - mref - bq) - kCodeShift, unorm16 units
   };
-  // The e4m3 code of P = 2^x, x = S cs - mref - bq, is the saturating
-  // round-to-nearest byte of 8 (x + 7) - kCodeShift = S cs8 + bias: one FMA
-  // and one convert per score, no exponential (a superchunk's largest x is
+  // The e4m3 code of P = 2^x, x = S cs - mref - bq, is the round-to-nearest
+  // byte of c = 8 (x + 7) - kCodeShift, clamped at 0: y = S cs8 + bias is
+  // (256 c + 127.5) / 65535, whose unorm16 convert (clamped to [0, 1]) holds
+  // the code in its high byte.  One FMA per score, one packed convert per two
+  // and a byte permute per four, no exponential (a superchunk's largest x is
   // below 8, so the largest code is 0x78 = 256; masked scores give 0).
   auto sm8_exp = [&](const f32x16 (&Sn)[2], int q, int j, int nt, const float bias, i32x8& pk)
       __attribute__((always_inline)) {
@@ -694,12 +704,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     const float y1 = __builtin_fmaf(Sn[q][4 * j + 1], cs8[nt], bias);
     const float y2 = __builtin_fmaf(Sn[q][4 * j + 2], cs8[nt], bias);
     const float y3 = __builtin_fmaf(Sn[q][4 * j + 3], cs8[nt], bias);
-    // (every byte is written: y0's own register serves as the old value)
-    unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(y0, 0, __float_as_uint(y0));
-    w = __builtin_amdgcn_cvt_pk_u8_f32(y1, 1, w);
-    w = __builtin_amdgcn_cvt_pk_u8_f32(y2, 2, w);
-    w = __builtin_amdgcn_cvt_pk_u8_f32(y3, 3, w);
-    pk[4 * q + j] = (int)w;
+    const unsigned lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pknorm_u16(y0, y1));
+    const unsigned hi = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pknorm_u16(y2, y3));
+    // bytes 0-3 of the result: the high bytes of y0, y1 (lo) and y2, y3 (hi)
+    pk[4 * q + j] = (int)__builtin_amdgcn_perm(hi, lo, 0x07050301u);
   };
   // e4m3 1.0 in every byte: the A operand of the row-sum MFMA.  Defined by
   // vector moves so that it lives in vector registers (as a uniform constant
@@ -889,7 +897,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       lsum[nt] = 0.f;
       if constexpr (F8) {
         Lacc[nt] = f32x16{};
-        base8[nt] = (56.f - kCodeShift) - 8.f * mref[nt];
+        base8[nt] = __builtin_fmaf(-8.f * kU16, mref[nt], (56.f - kCodeShift) * kU16 + kU16Half);
         rmax[nt] = -INFINITY;
       }
     }
