@@ -43,6 +43,12 @@ BF16_LSE_ABS = 2e-2    # LSE tolerance, bf16 path
 FP8_LSE_ABS = 0.08
 
 
+# One record per check_blocks call (label, pairs checked, worst and last-block
+# errors, tolerance), printed by the session's terminal summary so that the
+# per-block figures show in quiet runs too.
+PARITY_LOG = []
+
+
 def block_errors(o, O, geo, hkv, blocks=None, lse=None, L=None):
     """Errors of every (query block, KV head) pair on its own: the rows of
     query block i (absolute id) and the G query heads of KV head h.
@@ -84,6 +90,10 @@ def check_blocks(o, O, geo, hkv, fp8=False, blocks=None, lse=None, L=None, label
     if lse is not None:
         msg += f", worst lse_err {max(e['lse_err'] for e in errs):.2e}"
     print(msg, flush=True)
+    PARITY_LOG.append(dict(label=label, pairs=len(errs), worst_rel_l2=wr["rel_l2"], worst_block=wr["block"],
+                           worst_head=wr["head"], worst_max_abs=wa["max_abs"], last_block=last,
+                           last_rel_l2=lastr, tol=tol, fp8=fp8,
+                           worst_lse=max(e["lse_err"] for e in errs) if lse is not None else None))
     bad = [e for e in errs if not (e["finite"] and e["rel_l2"] < tol and (fp8 or e["max_abs"] < BF16_MAX_ABS)
                                    and e["lse_err"] < lse_tol)]
     assert not bad, f"{len(bad)} of {len(errs)} (block, head) pairs over tolerance, first: {bad[:4]}"

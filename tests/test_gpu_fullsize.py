@@ -94,8 +94,8 @@ def test_fullsize_contiguous(gpu, workload, fp8, sparsity):
             q = prob.q[:, sl].double().numpy()
             k = prob.k[:, h:h + 1].double().numpy()
             v = prob.v[:, h:h + 1].double().numpy()
-        ref = _check_group(h, G, q, k, v, tau, b, idx_h[h], cnt_h[h], out_h[:, sl], lse_h[sl], fp8, h, workload,
-                           all_blocks=S <= 32768)
+        ref = _check_group(h, G, q, k, v, tau, b, idx_h[h], cnt_h[h], out_h[:, sl], lse_h[sl], fp8, h,
+                           f"{workload}@{sparsity:.2f}", all_blocks=S <= 32768)
         assert np.abs(pk_h[h] - ref["kbar"][0]).max() < 2e-5
 
 
@@ -125,4 +125,4 @@ def test_fullsize_paged_batch6(gpu):
             v = seq["v"][:, h:h + 1].double().numpy()
             nqb = A.geometry(q.shape[0], k.shape[0], b).nqb
             _check_group(h, G, q, k, v, tau, b, idx_h[s, h, :nqb], cnt_h[s, h, :nqb], out_h[cu[s]:cu[s + 1], sl],
-                         lse_h[cu[s]:cu[s + 1], sl].T, False, 100 * s + h, f"paged seq {s}")
+                         lse_h[cu[s]:cu[s + 1], sl].T, False, 100 * s + h, f"paged_batch6 seq {s}")
