@@ -305,9 +305,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   f32x16 O[C::MT][NT];
   f32x16 Lacc[F8 ? NT : 1];  // fp8: row sums of P, accumulated by MFMA
   float mref[NT], lsum[NT];
-  // fp8: 8 * logit scale and 56 - kCodeShift - 8 * mref (the code offset of
-  // the pass's reference), both in unorm16 units (times kU16, the offset
-  // plus kU16Half); the largest superchunk maximum above mref (log2 units)
+  // fp8: 8 * logit scale and 112 - kCodeShift - 8 * mref (the code offset
+  // of the pass's reference, before the superchunk's 8 fx), both in unorm16
+  // units (times kU16, the offset plus kU16Half); the largest superchunk maximum above mref (log2 units)
   // seen in the pass, which sets the exact reference of a rerun.
   float cs8[F8 ? NT : 1], base8[F8 ? NT : 1], rmax[F8 ? NT : 1];
   // rerun search step per row (log2 units; negative once bracketed)
@@ -690,7 +690,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     float fx = floorf(rel);
     fx = fminf(fmaxf(fx, -110.f), 120.f);
     bq = (int)fx - 7;
-    bias = __builtin_fmaf(-8.f * kU16, (float)bq, base8[nt]);  // code offset 8 (7 - mref - bq) - kCodeShift, unorm16 units
+    // code offset 8 (7 - mref - bq) - kCodeShift = base8 - 8 fx in unorm16
+    // units (fx is integral, so no integer-to-float convert is needed)
+    bias = __builtin_fmaf(-8.f * kU16, fx, base8[nt]);
   };
   // The e4m3 code of P = 2^x, x = S cs - mref - bq, is the round-to-nearest
   // byte of c = 8 (x + 7) - kCodeShift, clamped at 0: y = S cs8 + bias is
@@ -897,7 +899,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       lsum[nt] = 0.f;
       if constexpr (F8) {
         Lacc[nt] = f32x16{};
-        base8[nt] = __builtin_fmaf(-8.f * kU16, mref[nt], (56.f - kCodeShift) * kU16 + kU16Half);
+        base8[nt] = __builtin_fmaf(-8.f * kU16, mref[nt], (112.f - kCodeShift) * kU16 + kU16Half);
         rmax[nt] = -INFINITY;
       }
     }
