@@ -52,3 +52,33 @@ def test_subnormal_and_underflow_codes_are_small():
     v = oracle.e4m3_decode(_codes(x))
     assert np.all(v <= 2.0 ** -6 + 1e-12)
     assert np.all(np.abs(v - 2.0 ** x) <= 2.0 ** -6)
+
+
+def test_unorm16_route_gives_the_rounded_code():
+    # The kernel forms y = (256 c + 127.5) / 65535 with one fp32 FMA per
+    # score, converts two scores at a time to unorm16 (clamp to [0, 1], then
+    # round(65535 y)) and keeps the high byte of each.  That byte is the code
+    # c rounded to nearest and clamped to [0, 255]: exactly, away from the
+    # half-integers; within 1/256 of one, a convert that truncated instead of
+    # rounding would move the code by one step (the same error as a shift of
+    # the centring constant by 1/512).
+    c = np.linspace(-3.0, 124.0, 2_000_001)
+    y = ((256.0 * c + 127.5) / 65535.0).astype(np.float32)
+    u = np.clip(y.astype(np.float64), 0.0, 1.0) * 65535.0
+    hi_rne = (np.rint(u) // 256).astype(np.int64)
+    hi_trunc = (np.floor(u) // 256).astype(np.int64)
+    want = np.clip(np.rint(c), 0, 255).astype(np.int64)
+    frac = c - np.floor(c)
+    away = np.abs(frac - 0.5) > 1e-5
+    assert np.array_equal(hi_rne[away], want[away])
+    assert np.abs(hi_trunc - want).max() <= 1
+    assert np.all(np.abs(frac[hi_trunc != want] - 0.5) <= 1.0 / 256)
+    # the four high bytes gathered by the byte permute (selector 0x07050301
+    # over the pair words lo = (y0, y1), hi = (y2, y3)) are y0, y1, y2, y3 in
+    # byte order 0-3 of the P register
+    lo = np.uint32(0x12AB) | (np.uint32(0x34CD) << np.uint32(16))
+    hi = np.uint32(0x56EF) | (np.uint32(0x7801) << np.uint32(16))
+    src = [(int(lo) >> (8 * k)) & 0xFF for k in range(4)] + [(int(hi) >> (8 * k)) & 0xFF for k in range(4)]
+    sel = 0x07050301
+    word = sum(src[(sel >> (8 * k)) & 0xFF] << (8 * k) for k in range(4))
+    assert word == 0x78563412
