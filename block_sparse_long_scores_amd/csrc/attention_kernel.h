@@ -325,14 +325,23 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   const int Skm1 = g.Sk - 1;
   const int plog = a.kv.page_log2;
   const int* ptab = PG ? a.kv.page_table + (long)s * a.kv.max_pages : nullptr;
+  // true in the paged instance as a constant (the entry point rejects a NULL
+  // table), the pointer test in the contiguous one (where it folds away)
+  const bool paged = PG ? true : ptab != nullptr;
 
   // Paged caches: page ids of key block j, lane i holding the id of its i-th
   // page (a block spans BLK / page_size <= 64 pages; page_size divides BLK).
+  // The page-table branches below test `paged`, a constant in the paged
+  // instance: a run-time test of the pointer left a branch around every
+  // page-id read, and the wait the compiler puts before a read of freshly
+  // loaded ids was then repeated after each copy pair (both paths of each
+  // branch merge), so the first block of a tile was issued one copy round
+  // trip at a time.
   // They are loaded one block ahead of the K/V copies that use them, so that
   // no copy address waits on a load (vmcnt drains in order: a wait for the
   // page table would also wait for every copy already in flight).
   auto load_pids = [&](int j) __attribute__((always_inline)) -> int {
-    if (!ptab) return 0;
+    if (!paged) return 0;
     const int p0 = (j * BLK) >> plog;
     const int npg = max(1, BLK >> plog);
     return lane < npg ? ptab[min(p0 + lane, Skm1 >> plog)] : 0;
@@ -364,7 +373,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     dq_it = wave;
     dq_bb = bb;
     dq_pids = pids;
-    const long b0 = ptab ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + dq_kb0) * rowbytes + h * C::ROWB;
+    const long b0 = paged ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + dq_kb0) * rowbytes + h * C::ROWB;
     dq_kp = (const char*)a.kv.k + b0;
     dq_vp = (const char*)a.kv.v + b0;
   };
@@ -372,7 +381,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     if (dq_it >= C::NLD) return;
     const bool inrow = dq_byte < C::ROWB && dq_row <= dq_rlast;
     long off;
-    if (!ptab) {
+    if (!paged) {
       off = (unsigned)(min(dq_row, dq_rlast) * rowbytes + (inrow ? dq_byte : 0));
     } else {
       const int key = dq_kb0 + min(dq_row, dq_rlast);
@@ -407,8 +416,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
   // plus that 32-bit offset.  Other paged layouts and a sequence's last,
   // partial block take the cursor above.  Copy op k of the wave exists for
   // every wave when k < NLD / 4.
-  const bool dfast = nwaves == 4 && (!ptab || ((C::RS << plog) & 1023) == 0);
-  const int rowmask = ptab ? (1 << plog) - 1 : BLK - 1;
+  const bool dfast = nwaves == 4 && (!paged || ((C::RS << plog) & 1023) == 0);
+  const int rowmask = paged ? (1 << plog) - 1 : BLK - 1;
   unsigned* const dtab = (unsigned*)(smem + a.lds_dtab) + C::NPWP * tid;
   if (dfast) {
 #pragma unroll
@@ -423,7 +432,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
     }
   }
   auto issue_fast = [&](int j, int bb, int pids) __attribute__((always_inline)) {
-    const long b0 = ptab ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + (long)j * BLK) * rowbytes + h * C::ROWB;
+    const long b0 = paged ? (long)h * C::ROWB : ((long)s * a.seq.seqlen_k + (long)j * BLK) * rowbytes + h * C::ROWB;
     u32x4 offv[C::NPWP / 4];
 #pragma unroll
     for (int r = 0; r < C::NPWP / 4; ++r) offv[r] = lds_read_u32x4(dtab + 4 * r);
@@ -432,7 +441,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const int q, const 
       const int it = wave + 4 * k;
       if (k < C::NLD / 4 || it < C::NLD) {
         long pb = b0;
-        if (ptab) {  // page of the op's first row (every row of the op is in it)
+        if (paged) {  // page of the op's first row (every row of the op is in it)
           const int pi = min((1024 * it) / C::RS, BLK - 1) >> plog;
           pb += ((long)__builtin_amdgcn_readlane(pids, pi) << plog) * rowbytes;
         }
