@@ -240,6 +240,9 @@ fp2_status fp2_dense_prefill(const fp2_params* p, int32_t batch,
  *                  the new chunk included (its K/V must already be written).
  *                  Sequence s has q_len = cu[s+1] - cu[s] <= seqlens_k[s]; its
  *                  query row r sits at position seqlens_k[s] - q_len + r.
+ *                  q_len may be 0 (a slot with cached tokens and no new rows:
+ *                  it gets no output rows and no attention tiles, and the
+ *                  exported mask holds no row for it); seqlens_k[s] >= 1.
  *   max_seqlen_q, max_seqlen_k : host upper bounds of q_len and seqlens_k.
  *   k_cache, v_cache : [num_pages, page_size, Hkv, d] (in_dtype).
  *   page_size    : a power of two dividing block_size, at least

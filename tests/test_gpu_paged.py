@@ -54,6 +54,46 @@ def test_paged_matches_oracle_and_contiguous(gpu, d, b, page):
         assert torch.equal(o2, out[cu[s]:cu[s + 1]])
 
 
+@pytest.mark.parametrize("page", [64, 16])
+def test_paged_sequences_without_new_rows(gpu, page):
+    """Continuous-batch slots with cached tokens but no new rows (q_len 0, in
+    the middle and at the end of the batch): they get no output rows and no
+    tiles.  The other sequences match the oracle and equal, bit for bit, the
+    same call with the empty slots left out (each tile computes the same
+    values whatever else the launch holds)."""
+    hq, hkv, d, b = 8, 2, 128, 128
+    kv_lens = [1500, 900, 1024, 64]
+    q_lens = [700, 0, 300, 0]
+    print(f"[case] paged empty slots kv_lens={kv_lens} q_lens={q_lens} page={page}", flush=True)
+    pb = synth.make_paged(13, kv_lens, q_lens, hq, hkv, d, b, page_size=page)
+    tau = 0.8
+    p = gpu.make_params(hq, hkv, d, b, tau=tau)
+    q, kc, vc = pb.q.cuda(), pb.k_cache.cuda(), pb.v_cache.cuda()
+    out, (idx, cnt), lse = gpu.sparse_prefill_paged(
+        p, q, pb.cu_seqlens_q.cuda(), pb.seqlens_k.cuda(), max(q_lens), max(kv_lens), kc, vc,
+        pb.page_table.cuda(), export_mask=True, return_lse=True)
+    keep = [s for s in range(len(q_lens)) if q_lens[s] > 0]
+    cu2 = torch.tensor(np.concatenate([[0], np.cumsum([q_lens[s] for s in keep])]), dtype=torch.int32)
+    sk2 = torch.tensor([kv_lens[s] for s in keep], dtype=torch.int32)
+    out2, lse2 = gpu.sparse_prefill_paged(p, q, cu2.cuda(), sk2.cuda(), max(q_lens), max(kv_lens), kc, vc,
+                                          pb.page_table[keep].contiguous().cuda(), return_lse=True)
+    torch.cuda.synchronize()
+    assert out.shape[0] == sum(q_lens)
+    assert not torch.isnan(out).any(), "a canary (NaN) page was read"
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    cu = pb.cu_seqlens_q.numpy()
+    for s in keep:
+        seq = pb.seqs[s]
+        qn, kn, vn = f64(seq["q"]), f64(seq["k"]), f64(seq["v"])
+        ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, q_blocks=[])
+        geo = ref["geo"]
+        kept_gpu = kept_from_lists(idx[s, :, :geo.nqb], cnt[s, :, :geo.nqb], geo.nkb)
+        assert_mask_matches(kept_gpu, ref["kept"], ref["S"], ref["thr"])
+        O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+        check_blocks(f64(out[cu[s]:cu[s + 1]]), O, geo, hkv, lse=f64(lse[cu[s]:cu[s + 1]]).T, L=L,
+                     label=f"paged empty slots seq {s}")
+
+
 def test_paged_mixed_prefill_and_decode_rows(gpu):
     """One call mixing decode rows (a one-row new chunk after a cached prefix),
     a chunked prefill and a full prefill, as continuous batching issues them:
