@@ -66,6 +66,47 @@ def test_sink_and_diagonal_only(gpu, S, Sq, hq, hkv, d, b, fp8):
     check_blocks(f64(out), O, geo, hkv, fp8=fp8, blocks=blocks, lse=f64(lse[0]), L=L, label="sink+diagonal only")
 
 
+# the smallest problems: a single key (the sink block is the diagonal block),
+# one query row after a partial block, a partial first block, and five rows
+# straddling the first block boundary (two query blocks, two key blocks)
+@pytest.mark.parametrize("S,Sq,fp8", [(1, None, False), (100, 1, False), (37, None, False), (130, 5, False),
+                                      (1, None, True), (130, 5, True)])
+def test_smallest_problems(gpu, S, Sq, fp8):
+    hq, hkv, d, b = 8, 2, 128, 128
+    pr = synth.make_problem("planted", 4, S, hq, hkv, d, b, seqlen_q=Sq)
+    print(f"[case] smallest planted seed=4 Sk={S} Sq={Sq or S} fp8={fp8}", flush=True)
+    tau = 0.5
+    if fp8:
+        qc, qs = synth.quantize_e4m3(pr.q, 1)
+        kc, ks = synth.quantize_e4m3(pr.k, 1)
+        vc, vs = synth.quantize_e4m3(pr.v, 1)
+        q, k, v, qs_, ks_, vs_ = (t.cuda() for t in (qc, kc, vc, qs, ks, vs))
+        p = gpu.make_params(hq, hkv, d, b, tau=tau, fp8=True, q_scale=qs_, k_scale=ks_, v_scale=vs_)
+        qn = oracle.dequantize(qc.numpy(), qs.numpy(), 1)
+        kn = oracle.dequantize(kc.numpy(), ks.numpy(), 1)
+        vn = oracle.dequantize(vc.numpy(), vs.numpy(), 1)
+    else:
+        q, k, v = (t.cuda() for t in (pr.q, pr.k, pr.v))
+        p = gpu.make_params(hq, hkv, d, b, tau=tau)
+        qn, kn, vn = f64(pr.q), f64(pr.k), f64(pr.v)
+    idx, cnt, pk, pv = gpu.select_blocks(p, q, k, v)
+    out, lse = gpu.sparse_prefill(p, q, k, v, idx, cnt, pk, pv, return_lse=True)
+    dense, dlse = gpu.dense_prefill(p, q, k, v, return_lse=True)
+    torch.cuda.synchronize()
+    ref = A.sparse_prefill(qn, kn, vn, hkv, b, tau, q_blocks=[])
+    geo = ref["geo"]
+    kept_gpu = kept_from_lists(idx[0], cnt[0], geo.nkb)
+    band = A.score_band_mask(ref["S"], ref["thr"])
+    assert not ((kept_gpu != ref["kept"]) & ~band).any()
+    O, L = A.attend(qn, kn, vn, kept_gpu, ref["kbar"], ref["vbar"], ref["n_k"], hkv, b, 1 / math.sqrt(d), True)
+    check_blocks(f64(out), O, geo, hkv, fp8=fp8, lse=f64(lse[0]), L=L, label=f"smallest Sk={S}")
+    if geo.nkb == 1:
+        # one key block: it is both sink and diagonal, nothing is dropped, and
+        # the sparse call is the dense one bit for bit
+        assert kept_gpu.all()
+        assert torch.equal(out, dense) and torch.equal(lse, dlse)
+
+
 @pytest.mark.parametrize("Sk", [5000, 5121, 5120])
 def test_one_row_chunk_after_long_prefix(gpu, Sk):
     """A one-row chunk (decode-like row) at the end of a prefix, contiguous
